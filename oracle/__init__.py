@@ -1,0 +1,31 @@
+"""CPU oracle for the LongCat-Flash zero-computation-expert MoE layer.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously-correct
+reference that the HIP path is checked against. Only the test suite, the smoke
+check and the benchmark's CPU-baseline leg may import it; the product path
+never does, and the two share no code.
+
+Source of what is computed: "LongCat-Flash" (llm-wiki entity page), section
+2.1 "Zero-Computation Experts" (the MoE sum, the zero-expert identity, the
+expert-bias update and its symbols), section 2.3.2 (softmax gating), and the
+model table in section 1 "核心参数" (layer shape).
+"""
+
+from .lcmoe_oracle import (  # noqa: F401
+    bf16_bits_to_f64,
+    e4m3fn_value_table,
+    dequant_fp8_blocks,
+    router_logits,
+    selection_scores,
+    select_topk,
+    softmax_gates,
+    expert_counts,
+    permutation,
+    silu,
+    expert_ffn,
+    combine_given_routing,
+    route,
+    forward,
+    dense_masked_forward,
+    bias_update,
+)

@@ -1,0 +1,289 @@
+"""Plain CPU definition of the zero-computation-expert MoE layer (fp64).
+
+TEST INFRASTRUCTURE ONLY -- imported by tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the product path. It shares no code,
+table or constant with the HIP library.
+
+Every function follows a passage of the "LongCat-Flash" llm-wiki entity page
+(cited per function) or one of the readings listed where that page is silent:
+
+  R-bias   the expert bias enters selection only: s = fl32(z + b) on the fp32
+           router logit; the gates never see it.
+  R-gate   gates are one softmax over all N+Z unbiased logits, read at the
+           selected experts, not renormalised over the K chosen ones.
+  R-ffn    an FFN expert is SiLU-gated: W2 (silu(W1 x) * (W3 x)), with the
+           gate rows W1 stacked above the up rows W3 in one [2I, d] matrix.
+  R-tie    selection order is (score descending, expert index ascending);
+           -0 and +0 compare equal.
+  R-upd    the bias update is applied to the N FFN experts only, computed in
+           fp64 as mu*(K_e*T_all - N*T_i)/(K*N*T_all) and rounded once into
+           the fp32 bias.
+  R-fp8    fp8 weights are OCP E4M3FN codes with one fp32 scale per 128x128
+           block; the dequantised weight is fl32(q * s).
+
+Precision: all arithmetic on activations is fp64 except where a step is
+defined in fp32 (the selection score, the fp8 dequantised weight, the bias
+written back), where the fp32 rounding is reproduced explicitly.
+"""
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16) -> float64 values.
+
+    A bf16 value is the upper half of an IEEE binary32 word, so the decode is
+    exact: shift into the high half, reinterpret as fp32, widen.
+    """
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value_table():
+    """Value of each of the 256 OCP FP8 E4M3FN codes, from the format definition.
+
+    Layout S.EEEE.MMM, exponent bias 7. Exponent field 0 is subnormal
+    (value m/8 * 2^(1-7)); exponent 15 with mantissa 7 is NaN; the format has
+    no infinities (so exponent 15 with mantissa 0..6 is an ordinary normal).
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = sign * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def dequant_fp8_blocks(codes, scales, block=128):
+    """fp8 block-scaled weight -> fp32 weight, w = fl32(q * s)   (reading R-fp8).
+
+    codes:  uint8 [R, C]; scales: fp32 [R/block, C/block].
+    q is exact in fp32 (every E4M3 value is), so the fp32 product rounds once.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, C = codes.shape
+    assert R % block == 0 and C % block == 0
+    q = e4m3fn_value_table()[codes].astype(np.float32)
+    s = np.asarray(scales, dtype=np.float32)
+    assert s.shape == (R // block, C // block)
+    s_full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+    return (q * s_full).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Routing  ("LongCat-Flash", section 2.1: router picks K of the N+Z experts;
+#           bias update drives the mean FFN-expert count per token to K_e)
+# ----------------------------------------------------------------------------
+
+
+def router_logits(x, w_router):
+    """z[t, i] = sum_k W_r[i, k] * x[t, k], accumulated in fp64.
+
+    x: [T, d] (values), w_router: [E, d] (fp32 values). Returns fp64 [T, E].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    return x @ w.T
+
+
+def selection_scores(z32, bias):
+    """s = fl32(fl32(z) + b), with -0 mapped to +0   (readings R-bias, R-tie)."""
+    z32 = np.asarray(z32, dtype=np.float32)
+    b = np.asarray(bias, dtype=np.float32)
+    s = (z32 + b[None, :]).astype(np.float32)
+    s[s == 0] = np.float32(0.0)
+    return s
+
+
+def select_topk(z32, bias, k):
+    """Top-K experts per token under (score desc, index asc)   (section 2.1, R-tie).
+
+    z32: the fp32 router logits [T, E]; bias: fp32 [E].
+    Returns int32 [T, K] in selection order. Uses a full lexicographic sort,
+    which is independent of any partial-selection scheme.
+    """
+    s = selection_scores(z32, bias)
+    T, E = s.shape
+    assert 1 <= k <= E
+    index_key = np.broadcast_to(np.arange(E), (T, E))
+    # np.lexsort: the last key is primary.  Primary: -s ascending (s desc);
+    # secondary: expert index ascending.
+    order = np.lexsort((index_key, -s.astype(np.float64)), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def softmax_gates(z, idx):
+    """Gates g[t, k] = softmax(z[t, :])[idx[t, k]] over all E experts (R-gate).
+
+    "LongCat-Flash" section 2.3.2 names softmax gating spread over the experts;
+    section 2.1's sum runs over all N+Z experts with weights g_i. Computed in
+    fp64 with the usual max subtraction; not renormalised over the K chosen.
+    Returns (g [T, K] fp64, p [T, E] fp64).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    g = np.take_along_axis(p, np.asarray(idx, dtype=np.int64), axis=1)
+    return g, p
+
+
+def expert_counts(idx, n_experts):
+    """T_i = number of (token, slot) pairs routed to expert i, for all E experts.
+
+    "LongCat-Flash" section 2.1 defines T_i as the tokens routed to expert i;
+    a token picks an expert at most once, so tokens and slots coincide.
+    """
+    return np.bincount(np.asarray(idx).ravel(), minlength=n_experts).astype(np.int64)
+
+
+def permutation(idx, n_ffn):
+    """Counting-sort permutation of the FFN slots.
+
+    Slots are the flat positions j = t*K + k of idx. Returns
+      offsets     int64 [N+1]  exclusive prefix sum of the FFN expert counts,
+      perm        int64 [S]    FFN slot ids grouped by expert (expert ascending),
+                               slot id ascending inside a group,
+      row_of_slot int64 [T*K]  position of each slot in perm, -1 for slots that
+                               went to a zero-computation expert.
+    """
+    flat = np.asarray(idx, dtype=np.int64).ravel()
+    counts = np.array([np.count_nonzero(flat == e) for e in range(n_ffn)], dtype=np.int64)
+    offsets = np.zeros(n_ffn + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    groups = [np.nonzero(flat == e)[0] for e in range(n_ffn)]
+    perm = np.concatenate(groups) if groups else np.zeros(0, dtype=np.int64)
+    row_of_slot = np.full(flat.shape[0], -1, dtype=np.int64)
+    row_of_slot[perm] = np.arange(perm.shape[0])
+    return offsets, perm.astype(np.int64), row_of_slot
+
+
+# ----------------------------------------------------------------------------
+# Experts and the layer  ("LongCat-Flash" section 2.1: MoE(x_t) = sum over the
+#  N+Z experts of g_i E_i(x_t); a zero-computation expert returns x_t)
+# ----------------------------------------------------------------------------
+
+
+def silu(u):
+    """silu(u) = u / (1 + exp(-u))."""
+    with np.errstate(over="ignore"):
+        return u / (1.0 + np.exp(-u))
+
+
+def expert_ffn(x_rows, w13, w2):
+    """SiLU-gated FFN expert (reading R-ffn).
+
+    x_rows: [m, d]; w13: [2I, d] with gate rows [0, I) and up rows [I, 2I);
+    w2: [d, I]. Returns [m, d] = (silu(x W1^T) * (x W3^T)) W2^T in fp64.
+    """
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    w13 = np.asarray(w13, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    inter = w2.shape[1]
+    u = x_rows @ w13.T
+    h = silu(u[:, :inter]) * u[:, inter:]
+    return h @ w2.T
+
+
+def combine_given_routing(x, idx, g, n_ffn, get_expert, tokens=None):
+    """y_t = sum_k g[t,k] * (E_{idx[t,k]}(x_t) if idx[t,k] < N else x_t).
+
+    x: [T, d] fp64 values; idx/g: [T, K]; get_expert(e) -> (w13_e, w2_e).
+    tokens: optional subset of token indices to evaluate (others not computed);
+    returns y rows for `tokens` (all tokens when None), fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    g = np.asarray(g, dtype=np.float64)
+    if tokens is None:
+        tokens = np.arange(x.shape[0])
+    tokens = np.asarray(tokens)
+    y = np.zeros((tokens.shape[0], x.shape[1]), dtype=np.float64)
+    sub_idx = idx[tokens]
+    sub_g = g[tokens]
+    # Zero-computation experts: identity, no FLOPs beyond the gate scaling.
+    zero_mask = sub_idx >= n_ffn
+    y += (sub_g * zero_mask).sum(axis=1)[:, None] * x[tokens]
+    # FFN experts: evaluate each touched expert once on the tokens that chose it.
+    for e in np.unique(sub_idx[~zero_mask]):
+        rows, ks = np.nonzero(sub_idx == e)
+        w13_e, w2_e = get_expert(int(e))
+        out = expert_ffn(x[tokens[rows]], w13_e, w2_e)
+        y[rows] += sub_g[rows, ks][:, None] * out
+    return y
+
+
+def route(x, w_router, bias, k):
+    """Routing half of the layer: logits, selection, gates, counts.
+
+    Returns dict(z=fp64 [T,E], z32=fp32 [T,E], idx=int32 [T,K], g=fp64 [T,K],
+    p=fp64 [T,E], counts=int64 [E]).
+    """
+    z = router_logits(x, w_router)
+    z32 = z.astype(np.float32)
+    idx = select_topk(z32, bias, k)
+    g, p = softmax_gates(z, idx)
+    counts = expert_counts(idx, z.shape[1])
+    return dict(z=z, z32=z32, idx=idx, g=g, p=p, counts=counts)
+
+
+def forward(x, w_router, bias, k, n_ffn, get_expert):
+    """The whole layer: route, then combine over FFN and zero-computation experts.
+
+    Returns (y fp64 [T, d], routing dict from `route`).
+    """
+    r = route(x, w_router, bias, k)
+    y = combine_given_routing(x, r["idx"], r["g"], n_ffn, get_expert)
+    return y, r
+
+
+def dense_masked_forward(x, p_masked, n_ffn, get_expert):
+    """The same sum evaluated densely: every FFN expert on every token.
+
+    p_masked: [T, E] gate matrix, zero outside each token's selected experts.
+    y = sum_{i<N} p[:, i] * E_i(x) + (sum_{i>=N} p[:, i]) * x.
+    No permutation or gather: an independent evaluation of the MoE sum.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    p_masked = np.asarray(p_masked, dtype=np.float64)
+    y = p_masked[:, n_ffn:].sum(axis=1)[:, None] * x
+    for e in range(n_ffn):
+        w13_e, w2_e = get_expert(e)
+        y = y + p_masked[:, e][:, None] * expert_ffn(x, w13_e, w2_e)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# Expert-bias update  ("LongCat-Flash" section 2.1, the bias-adaptation law and
+#  its symbols: mu adaptation rate, K_e target FFN count, T_i tokens routed to
+#  expert i, T_all tokens in the global batch)
+# ----------------------------------------------------------------------------
+
+
+def bias_update(bias, counts, n_ffn, k, mu, k_e, t_all):
+    """One step of the bias law, for the N FFN experts only (reading R-upd).
+
+    delta_i = mu * (K_e/K * 1/N - T_i/(K*T_all)) is evaluated as the single
+    fraction mu*(K_e*T_all - N*T_i) / (K*N*T_all) in fp64 (same value over the
+    reals; exactly zero at the fixed point T_i = K_e*T_all/N), then
+    b_i <- fl32(b_i + delta_i). Zero-computation experts keep their bias.
+    Every operation below is one IEEE fp64 operation, in this order.
+    """
+    b = np.asarray(bias, dtype=np.float32).copy()
+    counts = np.asarray(counts)
+    den = float(k) * float(n_ffn) * float(t_all)
+    for i in range(n_ffn):
+        num = float(k_e) * float(t_all) - float(n_ffn) * float(counts[i])
+        delta = (float(mu) * num) / den
+        b[i] = np.float32(float(b[i]) + delta)
+    return b
