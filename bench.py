@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of the LongCat-Flash zero-computation-expert MoE layer on one MI355X.
+
+One step = one lcmoe_forward call (router, biased top-K, permutation, grouped
+SiLU-gated expert GEMMs, combine) on a resident batch of synthetic tokens at
+the model's layer shape (d_model 6144, 512 FFN + 256 zero-computation
+experts, K=12, expert intermediate 2048; "LongCat-Flash" llm-wiki entity
+page, section 1 table). The headline value is the prefill batch (T=8192,
+bf16); the decode batch (T=64, bf16) and the fp8-weight batch (T=16384) are
+measured in the same run and reported alongside.
+
+Per-stage kernel durations come from HIP events recorded between the
+library's launches on the same stream (lcmoe_forward_staged) inside the timed
+region. The CPU oracle is timed on a bounded sample of the prefill workload.
+Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MoE-layer tokens/sec at 1 GPU (decode & prefill); % HBM / MFMA roofline"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 MFMA (fp8 weights run bf16 MFMA)
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def make_event_sets(hip, n_sets, n_events):
+    sets = []
+    for _ in range(n_sets):
+        arr = (ctypes.c_void_p * n_events)()
+        for i in range(n_events):
+            ev = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+            arr[i] = ev
+        sets.append(arr)
+    return sets
+
+
+def stage_ms(hip, sets, n_stages):
+    out = np.zeros((len(sets), n_stages))
+    for s, arr in enumerate(sets):
+        for i in range(n_stages):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), arr[i], arr[i + 1]) == 0
+            out[s, i] = ms.value
+    return out.mean(axis=0)
+
+
+def kernel_work(cfg, counts):
+    """Algorithmic bytes and MFMA flops of each grouped-GEMM stage.
+
+    Per expert touched on a path, its weights once (bf16 2 B, fp8 1 B plus
+    scales); per routed row, the input row read once and the output row
+    written once. Gate/up: 2I*d weights, reads d, writes I per row; down:
+    d*I weights, reads I, writes d per row. Flops 2*rows*(weights).
+    """
+    N, d, I = cfg.n_ffn, cfg.d, cfg.inter
+    c = counts[:N].astype(np.int64)
+    sw = 1 if cfg.wdtype == "fp8" else 2
+    sc = (4 / (128 * 128)) if cfg.wdtype == "fp8" else 0.0
+    out = {}
+    for path, sel in (("small", (c >= 1) & (c <= 32)), ("large", c > 32)):
+        et, rows = int(sel.sum()), int(c[sel].sum())
+        out[f"gateup_{path}"] = dict(
+            bytes=et * 2 * I * d * (sw + sc) + rows * d * 2 + rows * I * 2,
+            flops=2.0 * rows * 2 * I * d, experts=et, rows=rows)
+        out[f"down_{path}"] = dict(
+            bytes=et * d * I * (sw + sc) + rows * I * 2 + rows * d * 2,
+            flops=2.0 * rows * I * d, experts=et, rows=rows)
+    return out
+
+
+def layer_bytes(cfg, counts, T):
+    """Whole-layer algorithmic bytes: touched experts' weights once, the router
+    weights once, x read once and y written once."""
+    N, d, I, E = cfg.n_ffn, cfg.d, cfg.inter, cfg.n_experts
+    sw = 1 if cfg.wdtype == "fp8" else 2
+    et = int((counts[:N] > 0).sum())
+    return et * 3 * I * d * sw + E * d * 4 + 2 * T * d * 2
+
+
+def measure(cfg, steps, warmup, hip):
+    import torch
+    from mixture_experts_layer_biased_amd import inputs, lcmoe
+
+    L = inputs.make_layer(cfg, "cuda")
+    x = inputs.make_tokens(cfg, "cuda")
+    shape = lcmoe.shape_of(cfg)
+    T = cfg.tokens
+    ws = lcmoe.workspace(shape, T)
+    out = dict(y=torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"),
+               idx=torch.empty(T, cfg.k, dtype=torch.int32, device="cuda"),
+               gate=torch.empty(T, cfg.k, dtype=torch.float32, device="cuda"),
+               counts=torch.empty(cfg.n_experts, dtype=torch.int32, device="cuda"))
+    nst = lcmoe.NUM_STAGES
+    sets = make_event_sets(hip, steps, nst + 1)
+
+    def step(ev=None):
+        lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"], L["w13_scale"],
+                      L["w2_scale"], ws=ws, out=out, stage_events=ev)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(steps):
+        step(sets[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_stage = stage_ms(hip, sets, nst)
+    for arr in sets:
+        for i in range(nst + 1):
+            hip.hipEventDestroy(arr[i])
+    counts = out["counts"].cpu().numpy()
+    ms = total_ms / steps
+    work = kernel_work(cfg, counts)
+    stages = {name: float(per_stage[i]) for i, name in enumerate(lcmoe.STAGES)}
+    gemm = [k for k in work if work[k]["rows"] > 0]
+    dom = max(gemm, key=lambda k: stages[k])
+    wk = work[dom]
+    dom_s = stages[dom] / 1e3
+    bound = "hbm" if wk["flops"] / wk["bytes"] < PEAK_BF16 / PEAK_HBM else "mfma"
+    if bound == "hbm":
+        ach, peak, unit = wk["bytes"] / dom_s / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        ach, peak, unit = wk["flops"] / dom_s / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
+    gemm_s = sum(stages[k] for k in work) / 1e3
+    gemm_flops = sum(w["flops"] for w in work.values())
+    gemm_bytes = sum(w["bytes"] for w in work.values())
+    lb = layer_bytes(cfg, counts, T)
+    res = dict(
+        tokens=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), wall_s=wall,
+        mean_ffn_experts_per_token=float(counts[: cfg.n_ffn].sum() / T),
+        touched_experts=int((counts[: cfg.n_ffn] > 0).sum()),
+        max_rows_per_expert=int(counts[: cfg.n_ffn].max()),
+        stages_ms=stages,
+        dominant_kernel=dom,
+        roofline=dict(bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
+                      traffic=None, algorithmic_bytes=wk["bytes"], flops=wk["flops"],
+                      kernel_ms=stages[dom]),
+        grouped_gemm=dict(ms=gemm_s * 1e3, mfma_frac=gemm_flops / gemm_s / PEAK_BF16,
+                          hbm_frac=gemm_bytes / gemm_s / PEAK_HBM),
+        layer=dict(algorithmic_bytes=lb, hbm_frac=lb / (ms / 1e3) / PEAK_HBM,
+                   mfma_frac=gemm_flops / (ms / 1e3) / PEAK_BF16),
+    )
+    return res, (L, x, out)
+
+
+def cpu_baseline(cfg, L, x, out, n_experts_sample):
+    """The oracle on a bounded sample of the same workload: the full router,
+    selection and gates for all T tokens, plus the SiLU-gated FFN of a sample
+    of touched experts on all their routed tokens; the expert part is scaled by
+    (touched experts / sampled experts)."""
+    import oracle
+    from tests.helpers import bf16_values, expert_getter
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    T = cfg.tokens
+    t0 = time.perf_counter()
+    xv = bf16_values(x)
+    r = oracle.route(xv, L["w_router"].cpu().numpy(), L["bias"].cpu().numpy(), cfg.k)
+    t_route = time.perf_counter() - t0
+    idx = r["idx"]
+    touched = [e for e in range(cfg.n_ffn) if (idx == e).any()]
+    sample = touched[:: max(1, len(touched) // n_experts_sample)][:n_experts_sample]
+    get = expert_getter(L, cfg.wdtype)
+    t1 = time.perf_counter()
+    for e in sample:
+        rows, ks = np.nonzero(idx == e)
+        w13, w2 = get(e)
+        _ = r["g"][rows, ks][:, None] * oracle.expert_ffn(xv[rows], w13, w2)
+    t_exp = time.perf_counter() - t1
+    est = t_route + t_exp * len(touched) / max(1, len(sample))
+    return dict(value=T / est, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"{cfg.name} workload (T={T}): router, selection and gates for all "
+                        f"tokens ({t_route:.1f} s) + SiLU-gated FFN of {len(sample)} of "
+                        f"{len(touched)} touched experts on all their routed tokens "
+                        f"({t_exp:.1f} s), expert time scaled by {len(touched)}/{len(sample)}"),
+                measured_s=t_route + t_exp)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
+                    help="measure a single configuration (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=24)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_biased_amd import inputs, lcmoe
+    lcmoe.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "no GPU visible"
+    hip = _hip()
+    results = {}
+    baseline = None
+    names = [args.only] if args.only else ["prefill", "decode", "fp8"]
+    for name in names:
+        cfg = inputs.CONFIGS[name]
+        res, keep = measure(cfg, args.steps, args.warmup, hip)
+        results[name] = res
+        print(f"[bench] {name}: {res['ms_per_step']:.3f} ms/step, "
+              f"{res['tokens_per_s']:.0f} tok/s, dominant {res['dominant_kernel']} "
+              f"{res['roofline']['frac']:.3f} of {res['roofline']['bound']}", file=sys.stderr,
+              flush=True)
+        if name == names[0] and not args.no_cpu_baseline:
+            baseline = cpu_baseline(cfg, keep[0], keep[1], keep[2], args.cpu_experts)
+        del keep
+        torch.cuda.empty_cache()
+
+    main_name = names[0]
+    m = results[main_name]
+    cfg = inputs.CONFIGS[main_name]
+    line = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wdtype == "bf16" else "fp8-e4m3 weights, bf16 MFMA",
+        "data": "synthetic",
+        "config": {"workload": (f"LongCat-shape MoE layer, {main_name} batch: T={cfg.tokens}, "
+                                f"d_model={cfg.d}, {cfg.n_ffn} FFN + {cfg.n_zero} zero experts, "
+                                f"K={cfg.k}, I={cfg.inter}, {cfg.wdtype} weights, fp32 router"),
+                   "tokens": cfg.tokens, "parallelism": "single GPU"},
+        "roofline": {k: m["roofline"][k] for k in ("bound", "achieved", "peak", "unit",
+                                                     "frac", "traffic")},
+        "dominant_kernel": m["dominant_kernel"],
+        "cpu_baseline": baseline,
+        "detail": results,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * lcmoe -- LongCat-Flash MoE layer with zero-computation experts, for MI355X
+ * (gfx950). C ABI of liblcmoe.so.
+ *
+ * The layer ("LongCat-Flash", llm-wiki entity page, section 2.1
+ * "Zero-Computation Experts"):
+ *
+ *   MoE(x_t) = sum_{i < N+Z} g_i * E_i(x_t),  E_i(x_t) = x_t for the Z
+ *   zero-computation experts, a SiLU-gated FFN for the N others;
+ *   the router picks K experts per token on logit + expert bias;
+ *   the bias follows  db_i = mu * (K_e/K * 1/N - T_i/(K * T_all)).
+ *
+ * Readings where the page is silent (applied by every entry point):
+ *   - the bias is added to the fp32 router logit for selection only;
+ *   - gates are softmax(z) over all N+Z unbiased logits, read at the K
+ *     selected experts, not renormalised;
+ *   - selection order is (score descending, expert index ascending), -0 == +0;
+ *   - the FFN expert is W2 (silu(W1 x) * (W3 x)) with W1 (gate) rows [0, I)
+ *     and W3 (up) rows [I, 2I) stacked in one [2I][d] matrix;
+ *   - the bias update changes only the N FFN experts.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to row-major contiguous arrays
+ *     owned by the caller. The library keeps no device memory between calls;
+ *     scratch space is the caller's workspace `ws` of `ws_bytes` bytes (at
+ *     least lcmoe_workspace_bytes(shape, T)).
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     Outputs are fully overwritten. Two calls that share a workspace must
+ *     be ordered (same stream); there is no global mutable state.
+ *   - Expert ids 0..N-1 are FFN experts, N..N+Z-1 zero-computation experts.
+ *   - bf16 tensors are passed as raw 16-bit storage (`const void*`).
+ *   - fp8 weights (LCMOE_W_FP8_E4M3_B128) are OCP E4M3FN codes (one byte
+ *     each) with one fp32 scale per 128x128 block of each expert matrix;
+ *     the weight value is fl32(code_value * scale).
+ *   - Arguments are validated before anything is enqueued; on failure the
+ *     status is returned and nothing runs. No C++ exception crosses the ABI
+ *     and the library never aborts.
+ *
+ * Status codes:
+ *   LCMOE_ERR_INVALID_ARG  null required pointer, T < 0, K < 1, K > N+Z,
+ *                          N < 1, Z < 0, bad dtype code, mu/k_e not finite.
+ *   LCMOE_ERR_UNSUPPORTED  K > 64, N+Z > 2048, d % 32 != 0, I % 32 != 0,
+ *                          fp8 with d % 128 or I % 128 != 0, a tensor
+ *                          pointer not 16-byte aligned, T*K >= 2^31.
+ *   LCMOE_ERR_WORKSPACE    ws is NULL or ws_bytes too small.
+ *   LCMOE_ERR_HIP          a HIP launch failed (hipGetLastError).
+ */
+#ifndef LCMOE_H
+#define LCMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCMOE_OK = 0,
+  LCMOE_ERR_INVALID_ARG = 1,
+  LCMOE_ERR_UNSUPPORTED = 2,
+  LCMOE_ERR_WORKSPACE = 3,
+  LCMOE_ERR_HIP = 4
+} lcmoe_status;
+
+typedef enum {
+  LCMOE_W_BF16 = 0,          /* expert weights in bf16                         */
+  LCMOE_W_FP8_E4M3_B128 = 1  /* E4M3FN codes + fp32 scale per 128x128 block    */
+} lcmoe_wdtype;
+
+/* Layer shape. Model table of "LongCat-Flash" (section 1): d_model 6144,
+ * 512 FFN experts, 256 zero-computation experts, 12 experts per token,
+ * expert intermediate size 2048. */
+typedef struct {
+  int32_t d_model;   /* d                                   */
+  int32_t n_ffn;     /* N: FFN experts                      */
+  int32_t n_zero;    /* Z: zero-computation experts         */
+  int32_t top_k;     /* K: experts per token, zero included */
+  int32_t d_expert;  /* I: FFN expert intermediate size     */
+  int32_t w_dtype;   /* lcmoe_wdtype                        */
+} lcmoe_shape;
+
+/* Workspace bytes needed by lcmoe_route / lcmoe_permute / lcmoe_forward for
+ * any T <= max_tokens. Pure host function, no HIP call. Returns 0 for an
+ * invalid or unsupported shape or max_tokens < 0. Non-decreasing in
+ * max_tokens. */
+size_t lcmoe_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens);
+
+/* Routing half of the layer ("LongCat-Flash" section 2.1: the router selects
+ * K of the N+Z experts per token; T_i counts the tokens routed to expert i).
+ *
+ *   x_bf16     [T][d]   bf16 layer input (read; upcast to fp32 exactly)
+ *   w_router   [E][d]   fp32 router weights, E = N+Z
+ *   bias       [E]      fp32 expert bias, read for selection only
+ *   topk_idx   [T][K]   int32 out: selected experts in selection order
+ *   topk_gate  [T][K]   fp32 out: softmax(z_t)[topk_idx]
+ *   counts     [E]      int32 out: T_i for every expert
+ *   logits_out [T][E]   fp32 out, optional (NULL to skip): router logits z
+ *
+ * z = x W_r^T is computed with exact fp32 products (W_r is split exactly
+ * into three bf16 planes, x is bf16) and fp32 accumulation. Selection uses
+ * s = fl32(z + b). T == 0: counts are zeroed, nothing else is written. */
+lcmoe_status lcmoe_route(const lcmoe_shape* shape, int32_t T,
+                         const void* x_bf16, const float* w_router,
+                         const float* bias,
+                         int32_t* topk_idx, float* topk_gate,
+                         int32_t* counts, float* logits_out,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Counting-sort permutation of the FFN slots of a routing (the per-expert
+ * grouping that feeds the grouped expert GEMMs). Slots are the flat
+ * positions j = t*K + k of topk_idx.
+ *
+ *   topk_idx    [T][K]  int32 in: expert ids, each in [0, E), distinct per row
+ *   counts      [E]     int32 out: T_i for every expert
+ *   offsets     [N+1]   int32 out: exclusive prefix sum of counts[0..N)
+ *   perm        [T*K]   int32 out: entries [0, S) hold the FFN slot ids grouped
+ *                       by expert, ascending inside a group (S = offsets[N]);
+ *                       entries [S, T*K) are set to -1
+ *   row_of_slot [T*K]   int32 out: position of slot j in perm, -1 when slot j
+ *                       went to a zero-computation expert
+ * Ids outside [0, E) give unspecified (but memory-safe) results. */
+lcmoe_status lcmoe_permute(const lcmoe_shape* shape, int32_t T,
+                           const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* row_of_slot,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer ("LongCat-Flash" section 2.1, the MoE sum with
+ * zero-computation experts): routing as lcmoe_route, the permutation as
+ * lcmoe_permute, the SiLU-gated expert FFNs over the FFN-routed tokens only
+ * (grouped GEMMs), and the weighted combine
+ *   y_t = sum_k g_tk * (E_{idx_tk}(x_t) if idx_tk < N else x_t)
+ * accumulated in fp32 in k order and rounded once to bf16.
+ *
+ *   w13        [N][2I][d]  bf16, or E4M3FN codes (fp8)
+ *   w13_scale  [N][2I/128][d/128] fp32 (fp8 only; NULL for bf16)
+ *   w2         [N][d][I]   bf16, or E4M3FN codes (fp8)
+ *   w2_scale   [N][d/128][I/128]  fp32 (fp8 only; NULL for bf16)
+ *   y_bf16     [T][d]      bf16 out
+ *   topk_idx, topk_gate, counts: as lcmoe_route (written)
+ *
+ * Intermediate precision: expert GEMMs accumulate in fp32; the SiLU product
+ * and the expert output are stored as bf16 before the next step. With fp8
+ * weights each weight is rounded once, fl32(q*s) -> bf16, in registers. The
+ * bias is never modified here. */
+lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T,
+                           const void* x_bf16, const float* w_router,
+                           const float* bias,
+                           const void* w13, const float* w13_scale,
+                           const void* w2, const float* w2_scale,
+                           void* y_bf16,
+                           int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stages of lcmoe_forward, in launch order (for lcmoe_forward_staged). */
+typedef enum {
+  LCMOE_STAGE_ROUTER = 0,     /* router logits                          */
+  LCMOE_STAGE_TOPK = 1,       /* biased top-K and gates                 */
+  LCMOE_STAGE_PERMUTE = 2,    /* histogram, scans, stable scatter        */
+  LCMOE_STAGE_GATEUP_SMALL = 3,  /* gate/up GEMM, experts with <= 32 rows */
+  LCMOE_STAGE_GATEUP_LARGE = 4,  /* gate/up GEMM, experts with > 32 rows  */
+  LCMOE_STAGE_DOWN_SMALL = 5,    /* down GEMM, experts with <= 32 rows    */
+  LCMOE_STAGE_DOWN_LARGE = 6,    /* down GEMM, experts with > 32 rows     */
+  LCMOE_STAGE_COMBINE = 7,    /* weighted combine + zero-expert identity */
+  LCMOE_NUM_STAGES = 8
+} lcmoe_stage;
+
+/* lcmoe_forward with stage timing for profiling harnesses: identical work,
+ * plus hipEventRecord(stage_events[i], stream) before stage i and
+ * stage_events[LCMOE_NUM_STAGES] after the last one (stage_events holds
+ * LCMOE_NUM_STAGES + 1 caller-created events; NULL records nothing). The
+ * events are recorded only once validation has passed. */
+lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T,
+                                  const void* x_bf16, const float* w_router,
+                                  const float* bias,
+                                  const void* w13, const float* w13_scale,
+                                  const void* w2, const float* w2_scale,
+                                  void* y_bf16,
+                                  int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                                  void* ws, size_t ws_bytes, hipStream_t stream,
+                                  hipEvent_t* stage_events);
+
+/* Expert-bias update ("LongCat-Flash" section 2.1, the bias-adaptation law;
+ * mu the adaptation rate, K_e the target FFN experts per token, T_i the
+ * tokens routed to expert i, T_all the tokens in the global batch):
+ *   for i < N:  b_i <- fl32(b_i + mu*(K_e*T_all - N*T_i) / (K*N*T_all)),
+ * evaluated in fp64 in exactly that order (no contraction); b_i for i >= N
+ * unchanged. One launch of N threads, ordered after routing by the stream.
+ *
+ *   t_all   tokens in the batch whose counts are passed (> 0)
+ *   counts  [E] int32 device, read
+ *   bias    [E] fp32 device, updated in place */
+lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
+                               const int32_t* counts, double mu, double k_e,
+                               float* bias, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char* lcmoe_status_str(lcmoe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCMOE_H */

@@ -1,0 +1,55 @@
+// Internal launcher interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcmoe {
+
+// Experts with 1..kSmallMaxRows routed rows run on the weight-streaming
+// (small-M) GEMM; larger ones on the LDS-tiled GEMM in M-tiles of at most
+// kBigTileRows rows.
+constexpr int kSmallMaxRows = 32;
+constexpr int kBigTileRows = 256;
+
+// Grouped GEMM tile widths (output columns per block).
+constexpr int kSmallColsGateUp = 64;   // H columns per small gate/up block
+constexpr int kSmallColsDown = 128;    // Y columns per small down block
+constexpr int kBigColsGateUp = 128;    // H columns per large gate/up block
+constexpr int kBigColsDown = 256;      // Y columns per large down block
+
+struct GemmArgs {
+  const void* w;           // expert weights [N][rows_total][kdim], bf16 or fp8 codes
+  const float* wscale;     // fp8: [N][rows_total/128][kdim/128]
+  const uint16_t* src;     // gate/up: x [T][d]; down: H [S][I]
+  const int* perm;         // FFN slot ids grouped by expert (gate/up gather)
+  const int* offsets;      // [N+1]
+  const int* counts;       // [E]
+  const int* small_list;   // experts on the small-M path
+  const int* mt_prefix;    // [N+1] M-tile prefix for the large-M path
+  const int* meta;         // [0] #small experts, [1] #large M-tiles, [2] S
+  uint16_t* out;           // gate/up: H [S][I]; down: Y [S][d]
+  int kdim;                // reduction length (d or I)
+  int n_out;               // output columns (I or d)
+  int rows_total;          // weight rows per expert (2I or d)
+  int topk;
+  int n_ffn;
+  int nslices;             // column blocks per expert
+};
+
+void launch_router(const uint16_t* x, const float* wr, float* zpart, int T, int E, int d,
+                   int ks, int kchunk, hipStream_t s);
+void launch_topk(const float* zpart, int ks, const float* bias, int T, int E, int K, int* idx,
+                 float* gate, float* logits_out, hipStream_t s);
+void launch_permute(const int* idx, int T, int K, int E, int N, int ntile,
+                    unsigned long long* masks, int* tilecnt, int* tileoff, int* counts,
+                    int* offsets, int* small_list, int* mt_prefix, int* meta, int* perm,
+                    int* row_of_slot, hipStream_t s);
+void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
+void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
+void launch_combine(const uint16_t* x, const uint16_t* Y, const int* idx, const float* gate,
+                    const int* row_of_slot, int T, int d, int K, uint16_t* y, hipStream_t s);
+void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, double k_e,
+                        float* bias, hipStream_t s);
+
+}  // namespace lcmoe

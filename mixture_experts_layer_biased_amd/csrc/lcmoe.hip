@@ -1,0 +1,341 @@
+// C-ABI host library: argument validation, workspace carving and the launch
+// sequence of the layer. Every entry point validates before enqueuing
+// anything, never throws across the ABI and never synchronises the stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "lcmoe.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace lcmoe;
+
+constexpr size_t kAlign = 256;
+
+struct Layout {
+  int ks = 1, kchunk = 0, ntile = 0;
+  long long smax = 0;
+  size_t zpart = 0, masks = 0, tilecnt = 0, tileoff = 0, offsets = 0, small_list = 0,
+         mt_prefix = 0, meta = 0, routing_end = 0, perm = 0, row_of_slot = 0, permute_end = 0,
+         H = 0, Y = 0, total = 0;
+};
+
+inline long long n_experts(const lcmoe_shape& s) { return (long long)s.n_ffn + s.n_zero; }
+
+lcmoe_status check_shape(const lcmoe_shape* s) {
+  if (s == nullptr) return LCMOE_ERR_INVALID_ARG;
+  if (s->n_ffn < 1 || s->n_zero < 0 || s->top_k < 1 || s->d_model < 1 || s->d_expert < 1)
+    return LCMOE_ERR_INVALID_ARG;
+  if (s->top_k > n_experts(*s)) return LCMOE_ERR_INVALID_ARG;
+  if (s->w_dtype != LCMOE_W_BF16 && s->w_dtype != LCMOE_W_FP8_E4M3_B128)
+    return LCMOE_ERR_INVALID_ARG;
+  if (s->top_k > 64 || n_experts(*s) > 2048) return LCMOE_ERR_UNSUPPORTED;
+  if (s->d_model % 32 != 0 || s->d_expert % 32 != 0) return LCMOE_ERR_UNSUPPORTED;
+  if (s->w_dtype == LCMOE_W_FP8_E4M3_B128 && (s->d_model % 128 != 0 || s->d_expert % 128 != 0))
+    return LCMOE_ERR_UNSUPPORTED;
+  return LCMOE_OK;
+}
+
+// Router split-K factor: enough blocks to cover the chip at small T.
+void router_splits(int T, int E, int d, int& ks, int& kchunk) {
+  const long long base = (long long)((T + 127) / 128) * ((E + 63) / 64);
+  const int nstages = (d + 63) / 64;
+  int k = base >= 256 ? 1 : (int)std::min<long long>(16, std::max<long long>(1, 512 / std::max<long long>(base, 1)));
+  k = std::min(k, std::max(1, nstages / 2));
+  const int st_per = (nstages + k - 1) / k;
+  kchunk = st_per * 64;
+  ks = (d + kchunk - 1) / kchunk;
+}
+
+Layout make_layout(const lcmoe_shape& s, int T) {
+  Layout L;
+  const long long E = n_experts(s), N = s.n_ffn, K = s.top_k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + kAlign - 1) / kAlign * kAlign;
+    return o;
+  };
+  router_splits(T, (int)E, s.d_model, L.ks, L.kchunk);
+  L.ntile = (T + 63) / 64;
+  L.zpart = take((size_t)L.ks * T * E * 4);
+  L.masks = take((size_t)L.ntile * E * 8);
+  L.tilecnt = take((size_t)L.ntile * E * 4);
+  L.tileoff = take((size_t)L.ntile * E * 4);
+  L.offsets = take((size_t)(N + 1) * 4);
+  L.small_list = take((size_t)N * 4);
+  L.mt_prefix = take((size_t)(N + 1) * 4);
+  L.meta = take(64);
+  L.routing_end = off;
+  L.perm = take((size_t)T * K * 4);
+  L.row_of_slot = take((size_t)T * K * 4);
+  L.permute_end = off;
+  L.smax = (long long)T * std::min(K, N);
+  L.H = take((size_t)L.smax * s.d_expert * 2);
+  L.Y = take((size_t)L.smax * s.d_model * 2);
+  L.total = off;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Carve the workspace: returns the aligned base or nullptr if too small.
+char* ws_base(void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr) return nullptr;
+  const uintptr_t b = ((uintptr_t)ws + kAlign - 1) & ~(uintptr_t)(kAlign - 1);
+  const size_t pad = b - (uintptr_t)ws;
+  if (ws_bytes < pad || ws_bytes - pad < need) return nullptr;
+  return reinterpret_cast<char*>(b);
+}
+
+// Status of the launches just enqueued (the sticky error is cleared before
+// the first launch of every entry point, see clear_hip_error).
+lcmoe_status hip_status() {
+  return hipGetLastError() == hipSuccess ? LCMOE_OK : LCMOE_ERR_HIP;
+}
+void clear_hip_error() { (void)hipGetLastError(); }
+
+// Record stage boundary `i` on the stream when the caller asked for it.
+void mark(hipEvent_t* ev, int i, hipStream_t st) {
+  if (ev != nullptr) (void)hipEventRecord(ev[i], st);
+}
+
+template <typename T>
+T* at(char* base, size_t off) {
+  return reinterpret_cast<T*>(base + off);
+}
+
+// Routing sequence shared by route and forward: router GEMM, top-K + gates,
+// histogram / scan / schedule (+ optional scatter).
+void enqueue_routing(const lcmoe_shape& s, int T, const Layout& L, char* base,
+                     const void* x, const float* wr, const float* bias, int32_t* idx,
+                     float* gate, int32_t* counts, float* logits_out, int32_t* offsets,
+                     int32_t* perm, int32_t* row_of_slot, hipStream_t st) {
+  const int E = (int)n_experts(s);
+  float* zpart = at<float>(base, L.zpart);
+  launch_router(static_cast<const uint16_t*>(x), wr, zpart, T, E, s.d_model, L.ks, L.kchunk, st);
+  launch_topk(zpart, L.ks, bias, T, E, s.top_k, idx, gate, logits_out, st);
+  launch_permute(idx, T, s.top_k, E, s.n_ffn, L.ntile, at<unsigned long long>(base, L.masks),
+                 at<int>(base, L.tilecnt), at<int>(base, L.tileoff), counts, offsets,
+                 at<int>(base, L.small_list), at<int>(base, L.mt_prefix), at<int>(base, L.meta),
+                 perm, row_of_slot, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lcmoe_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens) {
+  if (check_shape(shape) != LCMOE_OK || max_tokens < 0) return 0;
+  if ((long long)max_tokens * shape->top_k >= (1ll << 31)) return 0;
+  // The router split factor shrinks as T grows; take the maximum over all
+  // T <= max_tokens so the result is non-decreasing in max_tokens (splits
+  // are 1 beyond 32768 tokens, where the layout grows with T).
+  size_t best = make_layout(*shape, max_tokens).total;
+  const int lim = std::min<int>(max_tokens, 32768);
+  for (int t = 1; t <= lim; ++t) best = std::max(best, make_layout(*shape, t).total);
+  return best + kAlign;
+}
+
+lcmoe_status lcmoe_route(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                         const float* w_router, const float* bias, int32_t* topk_idx,
+                         float* topk_gate, int32_t* counts, float* logits_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (T < 0 || counts == nullptr) return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (x_bf16 == nullptr || w_router == nullptr || bias == nullptr ||
+                topk_idx == nullptr || topk_gate == nullptr))
+    return LCMOE_ERR_INVALID_ARG;
+  if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
+  const int E = (int)n_experts(*shape);
+  if (T == 0) {
+    if (hipMemsetAsync(counts, 0, (size_t)E * 4, stream) != hipSuccess) return LCMOE_ERR_HIP;
+    return LCMOE_OK;
+  }
+  if (!aligned16(x_bf16) || !aligned16(w_router)) return LCMOE_ERR_UNSUPPORTED;
+  const Layout L = make_layout(*shape, T);
+  char* base = ws_base(ws, ws_bytes, L.routing_end);
+  if (base == nullptr) return LCMOE_ERR_WORKSPACE;
+  clear_hip_error();
+  enqueue_routing(*shape, T, L, base, x_bf16, w_router, bias, topk_idx, topk_gate, counts,
+                  logits_out, at<int>(base, L.offsets), nullptr, nullptr, stream);
+  return hip_status();
+}
+
+lcmoe_status lcmoe_permute(const lcmoe_shape* shape, int32_t T, const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* row_of_slot, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (T < 0 || counts == nullptr || offsets == nullptr) return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (topk_idx == nullptr || perm == nullptr || row_of_slot == nullptr))
+    return LCMOE_ERR_INVALID_ARG;
+  if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
+  const int E = (int)n_experts(*shape);
+  if (T == 0) {
+    if (hipMemsetAsync(counts, 0, (size_t)E * 4, stream) != hipSuccess ||
+        hipMemsetAsync(offsets, 0, (size_t)(shape->n_ffn + 1) * 4, stream) != hipSuccess)
+      return LCMOE_ERR_HIP;
+    return LCMOE_OK;
+  }
+  const Layout L = make_layout(*shape, T);
+  char* base = ws_base(ws, ws_bytes, L.routing_end);
+  if (base == nullptr) return LCMOE_ERR_WORKSPACE;
+  clear_hip_error();
+  launch_permute(topk_idx, T, shape->top_k, E, shape->n_ffn, L.ntile,
+                 at<unsigned long long>(base, L.masks), at<int>(base, L.tilecnt),
+                 at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.small_list),
+                 at<int>(base, L.mt_prefix), at<int>(base, L.meta), perm, row_of_slot, stream);
+  return hip_status();
+}
+
+lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                  const float* w_router, const float* bias, const void* w13,
+                                  const float* w13_scale, const void* w2, const float* w2_scale,
+                                  void* y_bf16, int32_t* topk_idx, float* topk_gate,
+                                  int32_t* counts, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, hipEvent_t* stage_events) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  const bool fp8 = shape->w_dtype == LCMOE_W_FP8_E4M3_B128;
+  if (T < 0 || counts == nullptr) return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (x_bf16 == nullptr || w_router == nullptr || bias == nullptr || w13 == nullptr ||
+                w2 == nullptr || y_bf16 == nullptr || topk_idx == nullptr ||
+                topk_gate == nullptr))
+    return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && fp8 && (w13_scale == nullptr || w2_scale == nullptr)) return LCMOE_ERR_INVALID_ARG;
+  if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
+  if (T == 0) {
+    if (hipMemsetAsync(counts, 0, (size_t)n_experts(*shape) * 4, stream) != hipSuccess)
+      return LCMOE_ERR_HIP;
+    return LCMOE_OK;
+  }
+  if (!aligned16(x_bf16) || !aligned16(w_router) || !aligned16(w13) || !aligned16(w2) ||
+      !aligned16(y_bf16))
+    return LCMOE_ERR_UNSUPPORTED;
+  const Layout L = make_layout(*shape, T);
+  char* base = ws_base(ws, ws_bytes, L.total);
+  if (base == nullptr) return LCMOE_ERR_WORKSPACE;
+  clear_hip_error();
+
+  int* offsets = at<int>(base, L.offsets);
+  int* perm = at<int>(base, L.perm);
+  int* row_of_slot = at<int>(base, L.row_of_slot);
+  const int E = (int)n_experts(*shape);
+  hipEvent_t* ev = stage_events;
+  mark(ev, 0, stream);
+  {
+    float* zpart = at<float>(base, L.zpart);
+    launch_router(static_cast<const uint16_t*>(x_bf16), w_router, zpart, T, E, shape->d_model,
+                  L.ks, L.kchunk, stream);
+    mark(ev, 1, stream);
+    launch_topk(zpart, L.ks, bias, T, E, shape->top_k, topk_idx, topk_gate, nullptr, stream);
+    mark(ev, 2, stream);
+    launch_permute(topk_idx, T, shape->top_k, E, shape->n_ffn, L.ntile,
+                   at<unsigned long long>(base, L.masks), at<int>(base, L.tilecnt),
+                   at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.small_list),
+                   at<int>(base, L.mt_prefix), at<int>(base, L.meta), perm, row_of_slot, stream);
+    mark(ev, 3, stream);
+  }
+
+  const int N = shape->n_ffn, d = shape->d_model, I = shape->d_expert;
+  uint16_t* H = at<uint16_t>(base, L.H);
+  uint16_t* Y = at<uint16_t>(base, L.Y);
+
+  // Grid bounds from what the host knows (no device->host sync): at most
+  // min(N, S) experts on the small path and S/256 + #large experts M-tiles.
+  const long long smax = L.smax;
+  const long long n_small_ub = std::min<long long>(N, smax);
+  const long long n_big_ub =
+      (smax + kBigTileRows - 1) / kBigTileRows + std::min<long long>(N, smax / (kSmallMaxRows + 1));
+  auto small_grid = [&](int nsl) {
+    return (int)std::max<long long>(1, std::min<long long>(n_small_ub * nsl, 512));
+  };
+  auto big_grid = [&](int nsl) {
+    const long long g = std::max<long long>(8, (n_big_ub * nsl + 7) / 8 * 8);
+    return (int)std::min<long long>(g, (1ll << 30));
+  };
+
+  GemmArgs a{};
+  a.offsets = offsets;
+  a.counts = counts;
+  a.small_list = at<int>(base, L.small_list);
+  a.mt_prefix = at<int>(base, L.mt_prefix);
+  a.meta = at<int>(base, L.meta);
+  a.perm = perm;
+  a.topk = shape->top_k;
+  a.n_ffn = N;
+
+  // gate/up: H = silu(X W1^T) * (X W3^T)
+  a.w = w13;
+  a.wscale = w13_scale;
+  a.src = static_cast<const uint16_t*>(x_bf16);
+  a.out = H;
+  a.kdim = d;
+  a.n_out = I;
+  a.rows_total = 2 * I;
+  a.nslices = (I + kSmallColsGateUp - 1) / kSmallColsGateUp;
+  launch_gemm_small(a, true, fp8, small_grid(a.nslices), stream);
+  mark(ev, 4, stream);
+  a.nslices = (I + kBigColsGateUp - 1) / kBigColsGateUp;
+  launch_gemm_big(a, true, fp8, big_grid(a.nslices), stream);
+  mark(ev, 5, stream);
+
+  // down: Y = H W2^T
+  a.w = w2;
+  a.wscale = w2_scale;
+  a.src = H;
+  a.out = Y;
+  a.kdim = I;
+  a.n_out = d;
+  a.rows_total = d;
+  a.nslices = (d + kSmallColsDown - 1) / kSmallColsDown;
+  launch_gemm_small(a, false, fp8, small_grid(a.nslices), stream);
+  mark(ev, 6, stream);
+  a.nslices = (d + kBigColsDown - 1) / kBigColsDown;
+  launch_gemm_big(a, false, fp8, big_grid(a.nslices), stream);
+  mark(ev, 7, stream);
+
+  launch_combine(static_cast<const uint16_t*>(x_bf16), Y, topk_idx, topk_gate, row_of_slot, T,
+                 d, shape->top_k, static_cast<uint16_t*>(y_bf16), stream);
+  mark(ev, 8, stream);
+  return hip_status();
+}
+
+lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                           const float* w_router, const float* bias, const void* w13,
+                           const float* w13_scale, const void* w2, const float* w2_scale,
+                           void* y_bf16, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  return lcmoe_forward_staged(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale,
+                              y_bf16, topk_idx, topk_gate, counts, ws, ws_bytes, stream, nullptr);
+}
+
+lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all, const int32_t* counts,
+                               double mu, double k_e, float* bias, hipStream_t stream) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (t_all <= 0 || counts == nullptr || bias == nullptr || !std::isfinite(mu) ||
+      !std::isfinite(k_e))
+    return LCMOE_ERR_INVALID_ARG;
+  clear_hip_error();
+  launch_bias_update(counts, shape->n_ffn, shape->top_k, t_all, mu, k_e, bias, stream);
+  return hip_status();
+}
+
+const char* lcmoe_status_str(lcmoe_status status) {
+  switch (status) {
+    case LCMOE_OK: return "LCMOE_OK";
+    case LCMOE_ERR_INVALID_ARG: return "LCMOE_ERR_INVALID_ARG";
+    case LCMOE_ERR_UNSUPPORTED: return "LCMOE_ERR_UNSUPPORTED";
+    case LCMOE_ERR_WORKSPACE: return "LCMOE_ERR_WORKSPACE";
+    case LCMOE_ERR_HIP: return "LCMOE_ERR_HIP";
+  }
+  return "LCMOE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

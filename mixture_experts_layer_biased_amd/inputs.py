@@ -99,6 +99,20 @@ def quantize_fp8_blocks(w):
     return codes, scale.to(torch.float32)
 
 
+def make_router(cfg, device):
+    """Router weights fp32 [E, d] ~ N(0, weight_std) and bias fp32 [E] (zeros,
+    or N(0, bias_std)); the same tensors make_layer returns for `cfg`."""
+    E, d = cfg.n_experts, cfg.d
+    w_router = torch.randn(E, d, generator=_gen(device, cfg.seed, 1), device=device,
+                           dtype=torch.float32) * cfg.weight_std
+    if cfg.bias_std > 0:
+        bias = torch.randn(E, generator=_gen(device, cfg.seed, 4), device=device,
+                           dtype=torch.float32) * cfg.bias_std
+    else:
+        bias = torch.zeros(E, device=device, dtype=torch.float32)
+    return w_router, bias
+
+
 def make_layer(cfg, device):
     """Router, bias and expert weights for `cfg` on `device`.
 
@@ -113,13 +127,7 @@ def make_layer(cfg, device):
     """
     E, d, N, I = cfg.n_experts, cfg.d, cfg.n_ffn, cfg.inter
     std = cfg.weight_std
-    w_router = torch.randn(E, d, generator=_gen(device, cfg.seed, 1), device=device,
-                           dtype=torch.float32) * std
-    if cfg.bias_std > 0:
-        bias = torch.randn(E, generator=_gen(device, cfg.seed, 4), device=device,
-                           dtype=torch.float32) * cfg.bias_std
-    else:
-        bias = torch.zeros(E, device=device, dtype=torch.float32)
+    w_router, bias = make_router(cfg, device)
     g13 = _gen(device, cfg.seed, 2)
     g2 = _gen(device, cfg.seed, 3)
     fp8 = cfg.wdtype == "fp8"

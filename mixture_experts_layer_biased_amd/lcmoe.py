@@ -1,0 +1,197 @@
+"""ctypes binding of liblcmoe.so over torch device tensors.
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Names follow the C ABI (include/lcmoe.h): route, permute, forward,
+bias_update, workspace_bytes. Work is enqueued on torch's current stream.
+If the library is missing, loading fails loudly; there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblcmoe.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+W_BF16, W_FP8_E4M3_B128 = 0, 1
+
+EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
+           "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_status_str")
+NUM_STAGES = 8
+STAGES = ("router", "topk", "permute", "gateup_small", "gateup_large", "down_small",
+          "down_large", "combine")
+
+
+class LcmoeError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_ffn", ctypes.c_int32),
+                ("n_zero", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_expert", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+
+    @property
+    def n_experts(self):
+        return self.n_ffn + self.n_zero
+
+
+def make_shape(d_model, n_ffn, n_zero, top_k, d_expert, w_dtype=W_BF16):
+    if isinstance(w_dtype, str):
+        w_dtype = {"bf16": W_BF16, "fp8": W_FP8_E4M3_B128}[w_dtype]
+    return Shape(d_model, n_ffn, n_zero, top_k, d_expert, w_dtype)
+
+
+def shape_of(cfg):
+    """Shape from a LayerConfig (mixture_experts_layer_biased_amd.inputs)."""
+    return make_shape(cfg.d, cfg.n_ffn, cfg.n_zero, cfg.k, cfg.inter, cfg.wdtype)
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib():
+    """Load liblcmoe.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                           "`python -m mixture_experts_layer_biased_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    S = ctypes.POINTER(Shape)
+    i32, sz, st = ctypes.c_int32, ctypes.c_size_t, ctypes.c_int
+    L.lcmoe_workspace_bytes.argtypes = [S, i32]
+    L.lcmoe_workspace_bytes.restype = sz
+    L.lcmoe_route.argtypes = [S, i32, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]
+    L.lcmoe_route.restype = st
+    L.lcmoe_permute.argtypes = [S, i32, _P, _P, _P, _P, _P, _P, sz, _P]
+    L.lcmoe_permute.restype = st
+    L.lcmoe_forward.argtypes = [S, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]
+    L.lcmoe_forward.restype = st
+    L.lcmoe_forward_staged.argtypes = [S, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       sz, _P, _P]
+    L.lcmoe_forward_staged.restype = st
+    L.lcmoe_bias_update.argtypes = [S, i32, _P, ctypes.c_double, ctypes.c_double, _P, _P]
+    L.lcmoe_bias_update.restype = st
+    L.lcmoe_status_str.argtypes = [st]
+    L.lcmoe_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(status):
+    return lib().lcmoe_status_str(status).decode()
+
+
+def _check(status, what):
+    if status != OK:
+        raise LcmoeError(status, f"{what}: {status_str(status)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA tensors"
+
+
+def workspace_bytes(shape, max_tokens):
+    return int(lib().lcmoe_workspace_bytes(ctypes.byref(shape), int(max_tokens)))
+
+
+def workspace(shape, max_tokens, device="cuda"):
+    n = workspace_bytes(shape, max_tokens)
+    if n == 0:
+        raise LcmoeError(ERR_INVALID_ARG, "invalid or unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def route(shape, x, w_router, bias, ws=None, logits=False, out=None):
+    """Router logits, biased top-K, gates and counts.
+
+    Returns dict(idx int32 [T,K], gate fp32 [T,K], counts int32 [E], logits fp32 [T,E] or None).
+    """
+    T = x.shape[0]
+    dev = x.device
+    K, E = shape.top_k, shape.n_experts
+    o = out or {}
+    idx = o.get("idx", torch.empty(T, K, dtype=torch.int32, device=dev))
+    gate = o.get("gate", torch.empty(T, K, dtype=torch.float32, device=dev))
+    counts = o.get("counts", torch.empty(E, dtype=torch.int32, device=dev))
+    lg = torch.empty(T, E, dtype=torch.float32, device=dev) if logits else None
+    if ws is None:
+        ws = workspace(shape, T, dev)
+    _dev(x, w_router, bias, idx, gate, counts, lg, ws)
+    _check(lib().lcmoe_route(ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                             _ptr(idx), _ptr(gate), _ptr(counts), _ptr(lg), _ptr(ws),
+                             ws.numel(), _stream()), "lcmoe_route")
+    return dict(idx=idx, gate=gate, counts=counts, logits=lg)
+
+
+def permute(shape, topk_idx, ws=None):
+    """Counting-sort permutation of the FFN slots of `topk_idx` [T,K] int32.
+
+    Returns dict(counts [E], offsets [N+1], perm [T*K], row_of_slot [T*K]), int32.
+    """
+    T = topk_idx.shape[0]
+    dev = topk_idx.device
+    K, E, N = shape.top_k, shape.n_experts, shape.n_ffn
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * K, dtype=torch.int32, device=dev)
+    row_of_slot = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev)
+    _dev(topk_idx, counts, offsets, perm, row_of_slot, ws)
+    _check(lib().lcmoe_permute(ctypes.byref(shape), T, _ptr(topk_idx), _ptr(counts),
+                               _ptr(offsets), _ptr(perm), _ptr(row_of_slot), _ptr(ws),
+                               ws.numel(), _stream()), "lcmoe_permute")
+    return dict(counts=counts, offsets=offsets, perm=perm, row_of_slot=row_of_slot)
+
+
+def forward(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, ws=None,
+            out=None, stage_events=None):
+    """The whole layer. Returns dict(y bf16 [T,d], idx, gate, counts).
+
+    stage_events: optional ctypes array of NUM_STAGES + 1 hipEvent_t handles
+    recorded at the stage boundaries (lcmoe_forward_staged)."""
+    T, d = x.shape
+    dev = x.device
+    K, E = shape.top_k, shape.n_experts
+    o = out or {}
+    y = o.get("y", torch.empty(T, d, dtype=torch.bfloat16, device=dev))
+    idx = o.get("idx", torch.empty(T, K, dtype=torch.int32, device=dev))
+    gate = o.get("gate", torch.empty(T, K, dtype=torch.float32, device=dev))
+    counts = o.get("counts", torch.empty(E, dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(shape, T, dev)
+    _dev(x, w_router, bias, w13, w2, w13_scale, w2_scale, y, idx, gate, counts, ws)
+    args = (ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13),
+            _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(idx), _ptr(gate),
+            _ptr(counts), _ptr(ws), ws.numel(), _stream())
+    if stage_events is None:
+        _check(lib().lcmoe_forward(*args), "lcmoe_forward")
+    else:
+        _check(lib().lcmoe_forward_staged(*args, stage_events), "lcmoe_forward_staged")
+    return dict(y=y, idx=idx, gate=gate, counts=counts)
+
+
+def bias_update(shape, counts, mu, k_e, bias, t_all):
+    """In-place bias update of the N FFN experts from `counts` of a T_all-token batch."""
+    _dev(counts, bias)
+    _check(lib().lcmoe_bias_update(ctypes.byref(shape), int(t_all), _ptr(counts),
+                                   float(mu), float(k_e), _ptr(bias), _stream()),
+           "lcmoe_bias_update")
+    return bias

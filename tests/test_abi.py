@@ -1,0 +1,134 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load and export every function declared in include/lcmoe.h;
+argument validation must return the documented status before any HIP call,
+so these run on a CPU-only host (fake, never-dereferenced device pointers).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_biased_amd import lcmoe
+from mixture_experts_layer_biased_amd.lcmoe import (ERR_INVALID_ARG, ERR_UNSUPPORTED,
+                                                    ERR_WORKSPACE, make_shape)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcmoe.h")
+
+FAKE = 0x10000           # 16-byte aligned, never dereferenced
+MIS = 0x10008            # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcmoe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = lcmoe.lib()
+    decl = declared_functions()
+    assert set(decl) == set(lcmoe.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+    # and the shared object's dynamic symbol table agrees
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", lcmoe.LIB_PATH],
+                         capture_output=True, text=True).stdout
+    syms = set(re.findall(r"\bT (lcmoe_\w+)", out))
+    assert set(decl) <= syms
+
+
+def test_status_strings():
+    assert lcmoe.status_str(0) == "LCMOE_OK"
+    assert lcmoe.status_str(3) == "LCMOE_ERR_WORKSPACE"
+
+
+def _route(shape, T, x=FAKE, wr=FAKE, b=FAKE, idx=FAKE, g=FAKE, c=FAKE, lg=None, ws=None, wsb=0):
+    L = lcmoe.lib()
+    return L.lcmoe_route(ctypes.byref(shape), T, x, wr, b, idx, g, c, lg, ws, wsb, None)
+
+
+def _forward(shape, T, x=FAKE, wr=FAKE, b=FAKE, w13=FAKE, s13=None, w2=FAKE, s2=None, y=FAKE,
+             idx=FAKE, g=FAKE, c=FAKE, ws=None, wsb=0):
+    L = lcmoe.lib()
+    return L.lcmoe_forward(ctypes.byref(shape), T, x, wr, b, w13, s13, w2, s2, y, idx, g, c,
+                           ws, wsb, None)
+
+
+GOOD = dict(d_model=64, n_ffn=8, n_zero=4, top_k=3, d_expert=32)
+
+
+def shp(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return make_shape(a["d_model"], a["n_ffn"], a["n_zero"], a["top_k"], a["d_expert"],
+                      a.get("w_dtype", 0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_ffn=0), ERR_INVALID_ARG),
+    (dict(n_zero=-1), ERR_INVALID_ARG),
+    (dict(top_k=0), ERR_INVALID_ARG),
+    (dict(top_k=13), ERR_INVALID_ARG),            # K > N+Z
+    (dict(w_dtype=7), ERR_INVALID_ARG),
+    (dict(n_ffn=100, top_k=65), ERR_UNSUPPORTED),  # K > 64
+    (dict(n_ffn=2000, n_zero=100), ERR_UNSUPPORTED),
+    (dict(d_model=48), ERR_UNSUPPORTED),
+    (dict(d_expert=40), ERR_UNSUPPORTED),
+    (dict(w_dtype=1), ERR_UNSUPPORTED),            # fp8 needs d, I % 128 == 0
+])
+def test_invalid_shapes(kw, status):
+    assert _route(shp(**kw), 4) == status
+    assert _forward(shp(**kw), 4) == status
+    assert lcmoe.workspace_bytes(shp(**kw), 4) == 0
+
+
+def test_invalid_arguments_route():
+    s = shp()
+    assert _route(s, -1) == ERR_INVALID_ARG
+    assert _route(s, 4, x=None) == ERR_INVALID_ARG
+    assert _route(s, 4, c=None) == ERR_INVALID_ARG
+    assert _route(s, 4, idx=None) == ERR_INVALID_ARG
+    assert _route(s, 4, x=MIS) == ERR_UNSUPPORTED
+    assert _route(s, 4, ws=None) == ERR_WORKSPACE
+    need = lcmoe.workspace_bytes(s, 4)
+    assert _route(s, 4, ws=FAKE, wsb=64) == ERR_WORKSPACE
+    assert need > 64
+    big = 2 ** 31 // 3 + 1
+    assert _route(s, big) == ERR_UNSUPPORTED       # T*K >= 2^31
+
+
+def test_invalid_arguments_forward_and_bias():
+    s = shp()
+    assert _forward(s, 4, w13=None) == ERR_INVALID_ARG
+    assert _forward(s, 4, y=None) == ERR_INVALID_ARG
+    assert _forward(s, 4, y=MIS) == ERR_UNSUPPORTED
+    assert _forward(s, 4, ws=FAKE, wsb=1024) == ERR_WORKSPACE
+    f = make_shape(128, 8, 4, 3, 128, 1)
+    assert _forward(f, 4) == ERR_INVALID_ARG        # fp8 without scales
+    L = lcmoe.lib()
+    assert L.lcmoe_bias_update(ctypes.byref(s), 0, FAKE, 1e-3, 2.0, FAKE, None) == ERR_INVALID_ARG
+    assert L.lcmoe_bias_update(ctypes.byref(s), 16, None, 1e-3, 2.0, FAKE, None) == ERR_INVALID_ARG
+    assert L.lcmoe_bias_update(ctypes.byref(s), 16, FAKE, float("nan"), 2.0, FAKE,
+                               None) == ERR_INVALID_ARG
+    assert L.lcmoe_permute(ctypes.byref(s), 4, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == ERR_INVALID_ARG
+    assert L.lcmoe_permute(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("dims", [
+    (64, 8, 4, 3, 32), (1024, 64, 32, 6, 512), (6144, 512, 256, 12, 2048)])
+def test_workspace_monotone(dims):
+    s = make_shape(*dims)
+    prev = 0
+    for T in [0, 1, 2, 15, 16, 63, 64, 65, 127, 128, 129, 1000, 4096, 8192, 16384, 32768]:
+        n = lcmoe.workspace_bytes(s, T)
+        assert n >= prev, (T, n, prev)
+        prev = n
+    # large-shape workspace is dominated by the H and Y spills: T*min(K,N)*(I+d)*2
+    d, N, Z, K, I = dims
+    assert lcmoe.workspace_bytes(s, 8192) >= 8192 * min(K, N) * (I + d) * 2

@@ -1,0 +1,124 @@
+"""GPU parity of the whole layer (routing, permutation, grouped SiLU-gated
+expert GEMMs, combine with the zero-expert identity) against the oracle.
+
+Tolerance (max relative error per token, infinity norm): 2e-2 with bf16
+weights, 5e-2 with fp8 weights, against the fp64 oracle evaluated on the
+GPU's own selection (selection parity is checked separately, bit-exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_biased_amd import inputs, lcmoe
+from tests.gpu_common import layer, max_rel_err, oracle_forward_rows
+from tests.helpers import bf16_values
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp8": 5e-2}
+
+
+def run_forward(cfg, L, x):
+    shape = lcmoe.shape_of(cfg)
+    res = lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"],
+                        L["w13_scale"], L["w2_scale"])
+    torch.cuda.synchronize()
+    return res
+
+
+def check_rows(cfg, L, x, res, tokens, cache=None):
+    idx = res["idx"].cpu().numpy()
+    y_ref = oracle_forward_rows(cfg, L, x, idx, tokens, cache=cache)
+    y = bf16_values(res["y"][torch.as_tensor(tokens, device=x.device)])
+    err = max_rel_err(y, y_ref)
+    print(f"{cfg.name} T={x.shape[0]}: max rel err {err:.3e} over {len(tokens)} tokens")
+    assert err < TOL[cfg.wdtype], err
+    return err
+
+
+def check_routing_consistent(cfg, L, x, res):
+    # forward's selection and counts are those of the routing entry point
+    r = lcmoe.route(lcmoe.shape_of(cfg), x, L["w_router"], L["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(r["idx"], res["idx"]) and torch.equal(r["gate"], res["gate"])
+    cnt = np.bincount(res["idx"].cpu().numpy().ravel(), minlength=cfg.n_experts)
+    assert np.array_equal(res["counts"].cpu().numpy(), cnt)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("tiny", 1), ("tiny", 200), ("tiny", 777),
+                                    ("small", 33), ("small", 300), ("small", 4096)])
+def test_forward_all_tokens(name, T):
+    # T spans the small-M path (few rows per expert), the mixed regime, and
+    # the large-M path with experts split into several M-tiles.
+    cfg, L = layer(name)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    res = run_forward(cfg, L, x)
+    check_routing_consistent(cfg, L, x, res)
+    check_rows(cfg, L, x, res, np.arange(T), cache={})
+
+
+def _sample(x, n, extra_large=0):
+    T = x.shape[0]
+    toks = list(np.linspace(0, T - 1, n).astype(int))
+    if extra_large:
+        norms = x.float().norm(dim=1)
+        toks += norms.topk(extra_large).indices.cpu().tolist()
+    return np.array(sorted(set(toks)))
+
+
+@pytest.mark.parametrize("name,n_sample,n_skew", [("decode", 8, 0), ("prefill", 6, 2),
+                                                  ("fp8", 5, 0)])
+def test_forward_longcat_shape_sampled(name, n_sample, n_skew):
+    cfg, L = layer(name)
+    x = inputs.make_tokens(cfg, "cuda")
+    res = run_forward(cfg, L, x)
+    check_routing_consistent(cfg, L, x, res)
+    counts = res["counts"].cpu().numpy()
+    print(f"{name}: mean FFN experts/token {counts[:cfg.n_ffn].sum() / cfg.tokens:.3f}, "
+          f"touched {int((counts[:cfg.n_ffn] > 0).sum())}, max rows {counts[:cfg.n_ffn].max()}")
+    check_rows(cfg, L, x, res, _sample(x, n_sample, n_skew))
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("small", 1000), ("decode", 64)])
+def test_closed_form_all_zero_routing_gpu(name, T):
+    # P-Y1: FFN experts biased out (K <= Z): y_t = (sum_k g_tk) x_t, rounded
+    # once to bf16 (unit roundoff 2^-8) from an fp32 accumulation.
+    cfg, L = layer(name)
+    b = L["bias"].clone()
+    b[: cfg.n_ffn] = -1e4
+    L2 = dict(L, bias=b)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    res = run_forward(cfg, L2, x)
+    idx = res["idx"].cpu().numpy()
+    assert np.all(idx >= cfg.n_ffn)
+    xv = bf16_values(x)
+    z = oracle.router_logits(xv, L["w_router"].cpu().numpy())
+    g, _ = oracle.softmax_gates(z, idx)
+    want = g.sum(1)[:, None] * xv
+    y = bf16_values(res["y"])
+    assert np.all(np.abs(y - want) <= 2.0 ** -8 * np.abs(want) + 1e-5 * np.abs(want).max())
+    # mirror: zero experts biased out -> no identity term
+    bm = L["bias"].clone()
+    bm[cfg.n_ffn:] = -1e4
+    res_m = run_forward(cfg, dict(L, bias=bm), x)
+    assert np.all(res_m["idx"].cpu().numpy() < cfg.n_ffn)
+    n = min(T, 8)
+    check_rows(cfg, dict(L, bias=bm), x, res_m, np.arange(n))
+
+
+def test_forward_zero_tokens_and_determinism():
+    cfg, L = layer("small")
+    shape = lcmoe.shape_of(cfg)
+    x0 = torch.empty(0, cfg.d, dtype=torch.bfloat16, device="cuda")
+    counts = torch.full((cfg.n_experts,), 3, dtype=torch.int32, device="cuda")
+    lcmoe.forward(shape, x0, L["w_router"], L["bias"], L["w13"], L["w2"],
+                  out=dict(counts=counts))
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0
+    # P-Y5: identical inputs give bitwise identical outputs
+    x = inputs.make_tokens(cfg, "cuda", tokens=2500)
+    a = run_forward(cfg, L, x)
+    b = run_forward(cfg, L, x)
+    for k in ("y", "idx", "gate", "counts"):
+        assert torch.equal(a[k], b[k]), k
