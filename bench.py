@@ -24,6 +24,10 @@ import time
 import numpy as np
 
 METRIC = "MoE-layer tokens/sec at 1 GPU (decode & prefill); % HBM / MFMA roofline"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "mixture_experts_layer_biased_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 4 << 30      # the calibration copy of copy_bandwidth()
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 MFMA (fp8 weights run bf16 MFMA)
 
@@ -35,6 +39,125 @@ def _hip():
                                         ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
     return lib
+
+
+def source_hash():
+    """Hash of the HIP sources: counter-derived traffic is used only while
+    the kernels are unchanged since the counters were taken."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stage_of_kernel(name):
+    """Map a kernel symbol to its forward stage name."""
+    if "gemm_big" in name:
+        return "gateup_large" if "<true" in name else "down_large"
+    if "gemm_small" in name:
+        return "gateup_small" if "<true" in name else "down_small"
+    for key, stage in (("router_gemm", "router"), ("topk", "topk"), ("combine", "combine"),
+                       ("hist_kernel", "permute"), ("colscan", "permute"),
+                       ("schedule_kernel", "permute"), ("scatter", "permute")):
+        if key in name:
+            return stage
+    return None
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from profiles/traffic.json, or None if
+    absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    e = t.get("workloads", {}).get(workload, {}).get(stage)
+    return None if e is None else e["bytes"]
+
+
+def pmc_summary(fetch_dir, write_dir, workload, cmd):
+    """Fold two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into profiles/traffic.json. Each counter is scaled by what it
+    reads for the 4 GiB device copy in the same run (true bytes / counted)."""
+    import csv
+    import collections
+
+    def per_kernel(d, counter):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        vals = collections.defaultdict(list)
+        copy = []
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+            else:
+                st = stage_of_kernel(r["Kernel_Name"])
+                if st:
+                    vals[(st, r["Kernel_Name"])].append(v)
+        calib = max(copy) if copy else None
+        return vals, calib
+
+    fv, fcal = per_kernel(fetch_dir, "FETCH_SIZE")
+    wv, wcal = per_kernel(write_dir, "WRITE_SIZE")
+    fscale = COPY_BYTES / fcal if fcal else 1.0
+    wscale = COPY_BYTES / wcal if wcal else 1.0
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    if t.get("source_hash") != source_hash():
+        t = {"workloads": {}}
+    t.update(source_hash=source_hash(), fetch_scale=fscale, write_scale=wscale,
+             calibration=f"FETCH_SIZE/WRITE_SIZE of a {COPY_BYTES >> 30} GiB device copy "
+                         f"read {COPY_BYTES / fscale / 2**30:.3f} / "
+                         f"{COPY_BYTES / wscale / 2**30:.3f} GiB")
+    wl = {}
+    for (st, kname), v in fv.items():
+        fb = float(np.mean(v)) * fscale
+        wb = float(np.mean(wv.get((st, kname), [0.0]))) * wscale
+        prev = wl.get(st)
+        if prev is None or fb + wb > prev["bytes"]:
+            wl[st] = dict(kernel=kname, fetch_bytes=fb, write_bytes=wb, bytes=fb + wb,
+                          dispatches=len(v))
+    t["workloads"][workload] = wl
+    t.setdefault("commands", {})[workload] = cmd
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+    print(json.dumps({k: {"bytes": v["bytes"], "kernel": v["kernel"][:60]} for k, v in wl.items()},
+                     indent=1))
+
+
+def trace_summary(trace_dir, workload, cmd, out_path):
+    """Write the rocprofv3 --kernel-trace --stats summary of the layer's
+    kernels (calls, average / min / max duration) as a markdown table."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics: {workload} workload", "",
+             "Command (from the repository root on the GPU host):", "", "```", cmd, "```", "",
+             "| kernel | stage | calls | average us | min us | max us | share % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        st = stage_of_kernel(name)
+        if st is None and "copyBuffer" not in name:
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {st or 'device copies (weight setup + 4 GiB calibration)'} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def make_event_sets(hip, n_sets, n_events):
@@ -154,14 +277,35 @@ def measure(cfg, steps, warmup, hip):
         stages_ms=stages,
         dominant_kernel=dom,
         roofline=dict(bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
-                      traffic=None, algorithmic_bytes=wk["bytes"], flops=wk["flops"],
-                      kernel_ms=stages[dom]),
+                      traffic=measured_traffic(cfg.name, dom), algorithmic_bytes=wk["bytes"],
+                      flops=wk["flops"], kernel_ms=stages[dom]),
         grouped_gemm=dict(ms=gemm_s * 1e3, mfma_frac=gemm_flops / gemm_s / PEAK_BF16,
                           hbm_frac=gemm_bytes / gemm_s / PEAK_HBM),
         layer=dict(algorithmic_bytes=lb, hbm_frac=lb / (ms / 1e3) / PEAK_HBM,
                    mfma_frac=gemm_flops / (ms / 1e3) / PEAK_BF16),
     )
     return res, (L, x, out)
+
+
+def copy_bandwidth(nbytes=4 << 30, reps=5):
+    """Achievable HBM bandwidth of a plain device-to-device copy (read + write
+    bytes per second), for reference next to the 8 TB/s peak."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def cpu_baseline(cfg, L, x, out, n_experts_sample):
@@ -208,8 +352,21 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
                     help="measure a single configuration (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=24)
+    ap.add_argument("--cpu-experts", type=int, default=160)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="fold rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="write a rocprofv3 --stats summary to profiles/")
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.cmd)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.workload, args.cmd,
+                      os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.md"))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -219,6 +376,8 @@ def main():
     lcmoe.lib()  # fail loudly if the HIP library is missing
     assert torch.cuda.is_available(), "no GPU visible"
     hip = _hip()
+    copy_gbps = copy_bandwidth()
+    print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read+write)", file=sys.stderr, flush=True)
     results = {}
     baseline = None
     names = [args.only] if args.only else ["prefill", "decode", "fp8"]
@@ -259,6 +418,7 @@ def main():
                                                      "frac", "traffic")},
         "dominant_kernel": m["dominant_kernel"],
         "cpu_baseline": baseline,
+        "copy_gbps": copy_gbps,
         "detail": results,
     }
     print(json.dumps(line))

@@ -94,11 +94,15 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// gfx950 LDS has 64 four-byte banks (256 bytes per cycle): a 16-byte-per-
+// lane access is conflict-free when each group of 16 lanes covers all 16
+// 16-byte bank slots of a 256-byte window.
+//
 // Swizzled offset (in 16-byte chunks) for an LDS tile whose rows are 8
-// chunks (128 bytes) wide: chunk c of row r lives at c ^ (r & 7), so eight
-// consecutive rows read at the same logical chunk hit distinct banks.
+// chunks (128 bytes) wide: chunk c of row r lives at c ^ ((r >> 1) & 7), so
+// sixteen consecutive rows read at the same logical chunk hit distinct slots.
 __device__ __forceinline__ int swz128(int row, int chunk) {
-  return row * 8 + (chunk ^ (row & 7));
+  return row * 8 + (chunk ^ ((row >> 1) & 7));
 }
 
 }  // namespace lcmoe

@@ -160,13 +160,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
   float z[J];
   uint64_t key[J];
   float zmax = -INFINITY;
+  // Split-K partial logits, summed in split order: all J loads of one split
+  // are issued together, splits follow each other.
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + 64 * j;
+    z[j] = e < E ? zpart[(size_t)t * E + e] : 0.f;
+  }
+  for (int s = 1; s < ks; ++s) {
+    const float* zs = zpart + ((size_t)s * T + t) * E;
+    float v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = (lane + 64 * j < E) ? zs[lane + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) z[j] += v[j];
+  }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     if (e < E) {
-      float v = zpart[(size_t)t * E + e];
-      for (int s = 1; s < ks; ++s) v += zpart[((size_t)s * T + t) * E + e];
-      z[j] = v;
+      const float v = z[j];
       if (logits_out) logits_out[(size_t)t * E + e] = v;
       float sc = v + bias[e];
       if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
