@@ -12,11 +12,11 @@
 //    into MFMA A-operand registers (v_mfma_f32_16x16x32_bf16, weights as the
 //    16-row side, tokens as the 16-column side staged in LDS). Weight bytes
 //    dominate; every weight of a touched expert is read once.
-//  * large-M (33+ rows, prefill batches): LDS-tiled, 256 token rows x 256
-//    weight rows x 64 k per stage, 8 waves (2 x 4), v_mfma_f32_32x32x16_bf16,
-//    each weight tile read once per M-tile; the M-tiles of an expert and
-//    its column slices are adjacent on one XCD (blockIdx % 8) so the x rows
-//    and repeated weight tiles are shared through that XCD's L2.
+//  * large-M (33+ rows, prefill batches): 256 token rows x 256 weight rows
+//    per block, 8 waves (2 x 4), v_mfma_f32_32x32x16_bf16, both operands
+//    copied HBM -> LDS by global_load_lds_dwordx4 in a multi-stage ring; the
+//    tiles of one expert (column slices, M-tiles) are adjacent on one XCD
+//    (blockIdx % 8) so its gathered x rows are shared through that XCD's L2.
 // fp8 (E4M3FN, one fp32 scale per 128x128 block) weights are converted in
 // registers: bf16(fl32(q) * s), then the same bf16 MFMA.
 #include <type_traits>
@@ -193,206 +193,33 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 }
 
 // ===========================================================================
-// large-M kernel
-// ===========================================================================
-constexpr int BK = 64;
-
-template <bool GATEUP, bool FP8>
-__global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
-  __shared__ uint4 sA[2][256 * 8];
-  __shared__ uint4 sB[2][256 * 8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int kdim = a.kdim;
-
-  // Tile order (expert, column slice, M-tile); each XCD takes a contiguous
-  // run of that order so neighbouring tiles share its L2.
-  const int total = a.meta[1] * a.nslices;
-  const int per = (total + 7) >> 3;
-  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
-  if (pos >= per) return;
-  const int L = xcd * per + pos;
-  if (L >= total) return;
-  int lo = 0, hi = a.n_ffn - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.mt_prefix[mid] * a.nslices <= L) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int mt = a.mt_prefix[e + 1] - a.mt_prefix[e];
-  const int local = L - a.mt_prefix[e] * a.nslices;
-  const int slice = local / mt, m = local - slice * mt;
-  const int cnt = a.counts[e];
-  const int r0 = (int)((long long)m * cnt / mt);
-  const int rows = (int)((long long)(m + 1) * cnt / mt) - r0;
-  const int rowbase = a.offsets[e] + r0;
-
-  // Per-thread load assignment: A and bf16 B: rows (tid>>3)+64u, chunk tid&7.
-  const int lc = tid & 7;
-  const uint16_t* asrc[4];
-  bool aval[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (tid >> 3) + 64 * u;
-    aval[u] = r < rows;
-    const int rr = aval[u] ? r : 0;
-    if (GATEUP)
-      asrc[u] = a.src + (size_t)(a.perm[rowbase + rr] / a.topk) * kdim + 8 * lc;
-    else
-      asrc[u] = a.src + (size_t)(rowbase + rr) * kdim + 8 * lc;
-  }
-  auto wrow_of = [&](int j) -> int {  // LDS B row -> weight row (or -1)
-    if (GATEUP) {
-      const int col = slice * kBigColsGateUp + (j & 127);
-      if (col >= a.n_out) return -1;
-      return j < 128 ? col : a.n_out + col;
-    } else {
-      const int col = slice * kBigColsDown + j;
-      return col < a.n_out ? col : -1;
-    }
-  };
-  constexpr int NB = FP8 ? 2 : 4;
-  const void* bsrc[NB];
-  bool bval[NB];
-  int bsblk[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const int j = FP8 ? (tid >> 2) + 128 * u : (tid >> 3) + 64 * u;
-    const int wr = wrow_of(j);
-    bval[u] = wr >= 0;
-    const size_t wrow = (size_t)e * a.rows_total + (bval[u] ? wr : 0);
-    bsblk[u] = (bval[u] ? wr : 0) >> 7;
-    if (FP8)
-      bsrc[u] = static_cast<const uint8_t*>(a.w) + wrow * kdim + 16 * (tid & 3);
-    else
-      bsrc[u] = static_cast<const uint16_t*>(a.w) + wrow * kdim + 8 * lc;
-  }
-
-  // Two register stages in flight (stage s lives in R[s & 1]) on top of the
-  // two LDS buffers: while stage s is multiplied out of LDS, stages s+1 and
-  // s+2 are on their way from memory.
-  uint4 ra[2][4], rb[2][NB];
-  auto load_stage = [&](int r, int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      ra[r][u] = (aval[u] && k0 + 8 * lc < kdim)
-                     ? *reinterpret_cast<const uint4*>(asrc[u] + k0)
-                     : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      if (FP8)
-        rb[r][u] = bval[u]
-                       ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(bsrc[u]) + k0)
-                       : make_uint4(0, 0, 0, 0);
-      else
-        rb[r][u] = (bval[u] && k0 + 8 * lc < kdim)
-                       ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(bsrc[u]) + k0)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_stage = [&](int r, int buf, int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sA[buf][swz128((tid >> 3) + 64 * u, lc)] = ra[r][u];
-    if (FP8) {
-      const int kblocks = kdim >> 7;
-      const size_t sbase = (size_t)e * (a.rows_total >> 7);
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int j = (tid >> 2) + 128 * u, c4 = tid & 3;
-        const float sc = bval[u] ? a.wscale[(sbase + bsblk[u]) * kblocks + (k0 >> 7)] : 0.f;
-        sB[buf][swz128(j, 2 * c4)] = fp8x8_scaled_to_bf16x8(rb[r][u].x, rb[r][u].y, sc);
-        sB[buf][swz128(j, 2 * c4 + 1)] = fp8x8_scaled_to_bf16x8(rb[r][u].z, rb[r][u].w, sc);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NB; ++u) sB[buf][swz128((tid >> 3) + 64 * u, lc)] = rb[r][u];
-    }
-  };
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
-
-  const int brow0 = GATEUP ? 32 * wn + (lane & 31) : 64 * wn + (lane & 31);
-  const int brow1 = GATEUP ? 128 + 32 * wn + (lane & 31) : 64 * wn + 32 + (lane & 31);
-  const int nst = (kdim + BK - 1) / BK;
-
-  auto compute_stage = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int chunk = 2 * s + (lane >> 5);
-      const bf16x8_t B0 = as_bf16x8(sB[buf][swz128(brow0, chunk)]);
-      const bf16x8_t B1 = as_bf16x8(sB[buf][swz128(brow1, chunk)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (wm * 128 + 32 * i < rows) {
-          const bf16x8_t A = as_bf16x8(sA[buf][swz128(wm * 128 + 32 * i + (lane & 31), chunk)]);
-          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc[i][0], 0, 0, 0);
-          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc[i][1], 0, 0, 0);
-        }
-      }
-    }
-  };
-  // One pipeline step: stage st computes from LDS[p], stage st+2 is requested
-  // into R[p], stage st+1 (requested one step earlier) moves R[q] -> LDS[q].
-  auto pipe_step = [&](int st, int p) {
-    const int q = p ^ 1;
-    if (st + 2 < nst) load_stage(p, (st + 2) * BK);
-    compute_stage(p);
-    if (st + 1 < nst) store_stage(q, q, (st + 1) * BK);
-    __syncthreads();
-  };
-
-  load_stage(0, 0);
-  if (nst > 1) load_stage(1, BK);
-  store_stage(0, 0, 0);
-  __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
-    pipe_step(st, 0);
-    if (st + 1 < nst) pipe_step(st + 1, 1);
-  }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (wm * 128 + 32 * i >= rows) continue;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tr = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (tr >= rows) continue;
-      uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
-      if (GATEUP) {
-        const int col = slice * kBigColsGateUp + 32 * wn + (lane & 31);
-        if (col < a.n_out) orow[col] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
-      } else {
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int col = slice * kBigColsDown + 64 * wn + 32 * f + (lane & 31);
-          if (col < a.n_out) orow[col] = f32_to_bf16(acc[i][f][v]);
-        }
-      }
-    }
-  }
-}
-
-// ===========================================================================
-// large-M kernel, bf16 weights: direct-to-LDS pipeline
+// large-M kernel: direct-to-LDS pipeline (bf16 or fp8 weights)
 //
-// Tile 256 token rows x 256 weight rows; the k loop runs in stages of 32.
-// Both operands move HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging), four LDS stages, three in flight while the fourth is multiplied.
-// LDS rows are 64 bytes (32 bf16); chunk c of row r is stored at
-// c ^ ((r >> 2) & 3), so the sixteen rows a 32x32x16 operand read touches
-// per LDS cycle land in distinct bank slots. A DMA instruction fills 16 rows
-// (1 KB): lane l writes row l/4, physical chunk l%4, and therefore loads
-// logical chunk (l%4) ^ ((row >> 2) & 3) of its row.
+// Tile up to 320 token rows x 256 weight rows; the k loop runs in stages of
+// 32. Both operands move HBM -> LDS with global_load_lds_dwordx4 (no
+// register staging) into a ring of LDS slots, all but one in flight while
+// one is multiplied. fp8 codes stay one byte in LDS and become
+// bf16(fl32(q) * s) in registers after the LDS read. The token rows form ten 32-row fragments,
+// fragment i belonging to wave row i & 1, so any row count splits evenly
+// over the two waves that share a SIMD.
+//
+// LDS layouts (16-byte chunks; gfx950 LDS has 64 banks, so each group of 16
+// lanes must touch 16 distinct 16-byte slots of a 256-byte window):
+//   x tile and bf16 weight tile: 64-byte rows, chunk c of row r at
+//     c ^ ((r >> 2) & 3);
+//   fp8 weight tile: 32-byte rows, chunk c of row r at c ^ ((r >> 3) & 1).
+// One copy instruction fills a contiguous 1 KB block: lane l writes the
+// block's l-th chunk, so it loads the logical chunk the swizzle puts there.
+//
+// k order inside a 32-wide stage (the same for both operands, as the MFMA
+// requires): bf16 weights: k-step ks and lane half h take k = 16 ks + 8 h
+// + [0, 8) (operand chunk 2 ks + h); fp8 weights: k = 16 h + 8 ks + [0, 8)
+// (x chunk 2 h + ks), so one 16-byte read of weight chunk h gives lane half
+// h its 16 codes for both k-steps.
 //
 // Each wave waits for its own copies of a stage (s_waitcnt vmcnt with the
-// count of its copies still allowed in flight) and a raw s_barrier then
-// publishes the stage to all waves; no fence that would drain the pipeline.
+// count of its younger copies still allowed in flight) and a raw s_barrier
+// then publishes the stage; no fence, which would drain the pipeline.
 // ===========================================================================
 constexpr int DBK = 32;  // k per pipeline stage
 
@@ -401,8 +228,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Wait until at most n (0..8) of this wave's vector memory operations remain.
-__device__ __forceinline__ void wait_vmcnt_upto8(int n) {
+// Wait until at most n (0..31) of this wave's vector memory operations remain.
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
   switch (n) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<1>(); break;
@@ -412,7 +239,30 @@ __device__ __forceinline__ void wait_vmcnt_upto8(int n) {
     case 5: wait_vmcnt<5>(); break;
     case 6: wait_vmcnt<6>(); break;
     case 7: wait_vmcnt<7>(); break;
-    default: wait_vmcnt<8>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break;
+    case 22: wait_vmcnt<22>(); break;
+    case 23: wait_vmcnt<23>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 25: wait_vmcnt<25>(); break;
+    case 26: wait_vmcnt<26>(); break;
+    case 27: wait_vmcnt<27>(); break;
+    case 28: wait_vmcnt<28>(); break;
+    case 29: wait_vmcnt<29>(); break;
+    case 30: wait_vmcnt<30>(); break;
+    default: wait_vmcnt<31>(); break;
   }
 }
 __device__ __forceinline__ void raw_barrier() {
@@ -433,16 +283,35 @@ __device__ __forceinline__ void dma16(const void* g, const uint4* lds) {
 __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * 4 + (chunk ^ ((row >> 2) & 3));
 }
+// 32-byte LDS rows (fp8 weight tile): chunk c of row r at c ^ ((r >> 3) & 1).
+__device__ __forceinline__ int swz32(int row, int chunk) {
+  return row * 2 + (chunk ^ ((row >> 3) & 1));
+}
 
-template <bool GATEUP>
+// The ring lives in one 144 KB LDS array. A slot holds the x rows of the
+// tile (16-row groups, 64 B per row) followed by the weight tile; the slot
+// count is what fits for the tile's actual row count, capped at 4 (bf16) or
+// 5 (fp8) stages.
+template <bool FP8>
+struct DmaTile {
+  static constexpr int LDS_CHUNKS = 9216;                  // 144 KB
+  static constexpr int MAX_SLOTS = FP8 ? 5 : 4;  // deeper rings measured no faster
+  static constexpr int B_CHUNKS = FP8 ? 256 * 2 : 256 * 4; // weight tile, 8 or 16 KB
+  static constexpr int AGROUPS = kBigTileRows / 16;        // 16-row copy groups of the x tile
+};
+
+template <bool GATEUP, bool FP8>
 __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
-  __shared__ uint4 sA0[1024], sA1[1024], sA2[1024], sA3[1024];
-  __shared__ uint4 sB0[1024], sB1[1024], sB2[1024], sB3[1024];
+  using TL = DmaTile<FP8>;
+  __shared__ uint4 lds[TL::LDS_CHUNKS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
+  const int h = lane >> 5;
   const int kdim = a.kdim;
 
+  // Tile order (expert, column slice, M-tile); each XCD takes a contiguous
+  // run of that order so neighbouring tiles share its L2.
   const int total = a.meta[1] * a.nslices;
   const int per_xcd = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
@@ -463,7 +332,7 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
   const int rows = (int)((long long)(m + 1) * cnt / mt) - r0;
   const int rowbase = a.offsets[e] + r0;
 
-  auto wrow_of = [&](int j) -> int {  // LDS B row -> weight row (or -1)
+  auto wrow_of = [&](int j) -> int {  // LDS weight-tile row -> weight row (or -1)
     if (GATEUP) {
       const int col = slice * kBigColsGateUp + (j & 127);
       if (col >= a.n_out) return -1;
@@ -474,63 +343,132 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
     }
   };
 
-  // Copy assignment: wave w fills row groups w and w+8 (16 rows each) of
-  // both operands; groups wholly outside the valid rows are skipped.
-  const uint16_t* w16 = static_cast<const uint16_t*>(a.w);
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
-  bool ause[2], buse[2];
+  // Copy assignment. x tile: wave w fills row groups w, w+8, w+16 (16 rows,
+  // 1 KB each). bf16 weights: groups w and w+8; fp8 weights: group w of 32
+  // rows (1 KB). Groups wholly outside the valid rows are skipped.
+  const uint16_t* asrc[3];
+  const char* bsrc[2];
+  bool ause[3], buse[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int g = wave + 8 * h;
+  for (int g2 = 0; g2 < 3; ++g2) {
+    const int g = wave + 8 * g2;
     const int row = 16 * g + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
-    ause[h] = 16 * g < rows;
+    ause[g2] = g < TL::AGROUPS && 16 * g < rows;
     const int rr = row < rows ? row : 0;
     if (GATEUP)
-      asrc[h] = a.src + (size_t)(a.perm[rowbase + rr] / a.topk) * kdim + 8 * c;
+      asrc[g2] = a.src + (size_t)(a.perm[rowbase + rr] / a.topk) * kdim + 8 * c;
     else
-      asrc[h] = a.src + (size_t)(rowbase + rr) * kdim + 8 * c;
-    buse[h] = wrow_of(16 * g) >= 0;
-    const int wr = wrow_of(row);
-    bsrc[h] = w16 + ((size_t)e * a.rows_total + (wr >= 0 ? wr : 0)) * kdim + 8 * c;
+      asrc[g2] = a.src + (size_t)(rowbase + rr) * kdim + 8 * c;
   }
-  const int per_stage = (int)ause[0] + (int)ause[1] + (int)buse[0] + (int)buse[1];
+  if (FP8) {
+    const int row = 32 * wave + (lane >> 1);
+    const int c = (lane & 1) ^ ((row >> 3) & 1);
+    const int wr = wrow_of(row);
+    buse[0] = wrow_of(32 * wave) >= 0;
+    buse[1] = false;
+    bsrc[0] = static_cast<const char*>(a.w) + ((size_t)e * a.rows_total + (wr >= 0 ? wr : 0)) * kdim + 16 * c;
+    bsrc[1] = bsrc[0];
+  } else {
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const int g = wave + 8 * g2;
+      const int row = 16 * g + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int wr = wrow_of(row);
+      buse[g2] = wrow_of(16 * g) >= 0;
+      bsrc[g2] = static_cast<const char*>(a.w) +
+                 (((size_t)e * a.rows_total + (wr >= 0 ? wr : 0)) * kdim + 8 * c) * 2;
+    }
+  }
+  const int per_stage =
+      (int)ause[0] + (int)ause[1] + (int)ause[2] + (int)buse[0] + (int)buse[1];
   const int nst = kdim / DBK;
+  // Ring geometry for this tile (wave-uniform).
+  const int a_chunks = ((rows + 15) >> 4) * 64;
+  const int slot = a_chunks + TL::B_CHUNKS;
+  const int nslots = min(TL::MAX_SLOTS, TL::LDS_CHUNKS / slot);
 
-  auto issue = [&](int s, uint4* A, uint4* B) {
+  auto issue = [&](int s) {
     const int k0 = s * DBK;
-    if (ause[0]) dma16(asrc[0] + k0, A + wave * 64);
-    if (ause[1]) dma16(asrc[1] + k0, A + (wave + 8) * 64);
-    if (buse[0]) dma16(bsrc[0] + k0, B + wave * 64);
-    if (buse[1]) dma16(bsrc[1] + k0, B + (wave + 8) * 64);
+    const uint4* base = lds + (s % nslots) * slot;
+    if (ause[0]) dma16(asrc[0] + k0, base + wave * 64);
+    if (ause[1]) dma16(asrc[1] + k0, base + (wave + 8) * 64);
+    if (ause[2]) dma16(asrc[2] + k0, base + (wave + 16) * 64);
+    if (FP8) {
+      if (buse[0]) dma16(bsrc[0] + k0, base + a_chunks + wave * 64);
+    } else {
+      if (buse[0]) dma16(bsrc[0] + 2 * k0, base + a_chunks + wave * 64);
+      if (buse[1]) dma16(bsrc[1] + 2 * k0, base + a_chunks + (wave + 8) * 64);
+    }
   };
 
-  f32x16_t acc[4][2];
+  constexpr int MF = kBigTileRows / 64;  // fragments per wave (5)
+  f32x16_t acc[MF][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
+  // Token row of this wave's j-th fragment: fragment 2j + wm.
+  auto frow = [&](int j) { return 32 * (2 * j + wm); };
 
-  const int brow0 = GATEUP ? 32 * wn + (lane & 31) : 64 * wn + (lane & 31);
-  const int brow1 = GATEUP ? 128 + 32 * wn + (lane & 31) : 64 * wn + 32 + (lane & 31);
-  // 32-row fragments of this wave that hold routed rows (wave-uniform).
-  const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, (rows - wm * 128 + 31) / 32)));
-  // Multiply one stage: all LDS operand reads of both k-steps first, then
-  // the MFMAs, so the reads overlap instead of waiting one by one.
-  auto compute_n = [&](auto NA_c, const uint4* A, const uint4* B) {
+  const int bbase0 = GATEUP ? 32 * wn : 64 * wn;
+  const int bbase1 = GATEUP ? 128 + 32 * wn : 64 * wn + 32;
+  const int brow0 = bbase0 + (lane & 31), brow1 = bbase1 + (lane & 31);
+  // fp8: the two weight fragments' block scales for every 128-wide k block,
+  // loaded once before the k loop (lane l holds blocks l and l+64) and read
+  // per stage with v_readlane, so the loop issues no memory op besides the
+  // copies it counts.
+  const int kblocks = kdim >> 7;
+  int scv[2][2] = {{0, 0}, {0, 0}};
+  if (FP8) {
+    const int wr0 = wrow_of(bbase0), wr1 = wrow_of(bbase1);
+    const float* sr0 = a.wscale + ((size_t)e * (a.rows_total >> 7) + (wr0 >= 0 ? wr0 >> 7 : 0)) * kblocks;
+    const float* sr1 = a.wscale + ((size_t)e * (a.rows_total >> 7) + (wr1 >= 0 ? wr1 >> 7 : 0)) * kblocks;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kb = lane + 64 * j;
+      scv[0][j] = (wr0 >= 0 && kb < kblocks) ? __float_as_int(sr0[kb]) : 0;
+      scv[1][j] = (wr1 >= 0 && kb < kblocks) ? __float_as_int(sr1[kb]) : 0;
+    }
+  }
+  wait_vmcnt<0>();  // every load before the copies has landed
+  // 32-row fragments of this wave that hold routed rows (wave-uniform):
+  // fragments 2j + wm with 32 (2j + wm) < rows.
+  const int nact = __builtin_amdgcn_readfirstlane(
+      max(0, min(MF, (rows - 32 * wm + 63) / 64)));
+
+  // Multiply one stage: all LDS operand reads first, then the MFMAs.
+  auto compute_n = [&](auto NA_c, int s) {
     constexpr int NA = decltype(NA_c)::value;
+    const uint4* A = lds + (s % nslots) * slot;
+    const uint4* B = A + a_chunks;
     bf16x8_t Bv[2][2], Av[2][NA > 0 ? NA : 1];
+    if (FP8) {
+      const uint4 q0 = B[swz32(brow0, h)];
+      const uint4 q1 = B[swz32(brow1, h)];
+      const int kb = (s * DBK) >> 7;
+      const float s0 = __int_as_float(__builtin_amdgcn_readlane(scv[0][kb >> 6], kb & 63));
+      const float s1 = __int_as_float(__builtin_amdgcn_readlane(scv[1][kb >> 6], kb & 63));
+      Bv[0][0] = as_bf16x8(fp8x8_scaled_to_bf16x8(q0.x, q0.y, s0));
+      Bv[1][0] = as_bf16x8(fp8x8_scaled_to_bf16x8(q0.z, q0.w, s0));
+      Bv[0][1] = as_bf16x8(fp8x8_scaled_to_bf16x8(q1.x, q1.y, s1));
+      Bv[1][1] = as_bf16x8(fp8x8_scaled_to_bf16x8(q1.z, q1.w, s1));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Bv[ks][0] = as_bf16x8(B[swz64(brow0, 2 * ks + h)]);
+        Bv[ks][1] = as_bf16x8(B[swz64(brow1, 2 * ks + h)]);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
-      Bv[ks][0] = as_bf16x8(B[swz64(brow0, c)]);
-      Bv[ks][1] = as_bf16x8(B[swz64(brow1, c)]);
+      const int c = FP8 ? 2 * h + ks : 2 * ks + h;
 #pragma unroll
       for (int i = 0; i < NA; ++i)
-        Av[ks][i] = as_bf16x8(A[swz64(wm * 128 + 32 * i + (lane & 31), c)]);
+        Av[ks][i] = as_bf16x8(A[swz64(frow(i) + (lane & 31), c)]);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -540,28 +478,20 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
         acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[ks][i], Bv[ks][1], acc[i][1], 0, 0, 0);
       }
   };
-  // Stage s: wait for its copies (stages s+1, s+2 may stay in flight),
-  // publish, queue stage s+3 into the buffer freed by stage s-1, multiply.
-  // The loop is instantiated per active-fragment count so each variant is
-  // straight-line code.
+  // Stage s: wait for its copies (younger stages stay in flight), publish,
+  // queue stage s+nslots-1 into the slot freed by stage s-1, multiply. The
+  // loop is instantiated per active-fragment count (straight-line code).
   auto kloop = [&](auto NA_c) {
-    auto step = [&](int s, const uint4* A, const uint4* B, uint4* An, uint4* Bn) {
-      wait_vmcnt_upto8(per_stage * min(2, nst - 1 - s));
+    for (int s = 0; s < nslots - 1 && s < nst; ++s) issue(s);
+    for (int s = 0; s < nst; ++s) {
+      wait_vmcnt_upto(per_stage * min(nslots - 2, nst - 1 - s));
       raw_barrier();
-      if (s + 3 < nst) issue(s + 3, An, Bn);
-      compute_n(NA_c, A, B);
-    };
-    issue(0, sA0, sB0);
-    if (nst > 1) issue(1, sA1, sB1);
-    if (nst > 2) issue(2, sA2, sB2);
-    for (int s = 0; s < nst; s += 4) {
-      step(s, sA0, sB0, sA3, sB3);
-      if (s + 1 < nst) step(s + 1, sA1, sB1, sA0, sB0);
-      if (s + 2 < nst) step(s + 2, sA2, sB2, sA1, sB1);
-      if (s + 3 < nst) step(s + 3, sA3, sB3, sA2, sB2);
+      if (s + nslots - 1 < nst) issue(s + nslots - 1);
+      compute_n(NA_c, s);
     }
   };
   switch (nact) {
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
     case 4: kloop(std::integral_constant<int, 4>{}); break;
     case 3: kloop(std::integral_constant<int, 3>{}); break;
     case 2: kloop(std::integral_constant<int, 2>{}); break;
@@ -570,11 +500,11 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (wm * 128 + 32 * i >= rows) continue;
+  for (int i = 0; i < MF; ++i) {
+    if (frow(i) >= rows) continue;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int tr = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int tr = frow(i) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (tr >= rows) continue;
       uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
       if (GATEUP) {
@@ -606,11 +536,11 @@ void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipSt
 
 void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s) {
   if (gateup) {
-    if (fp8) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(a);
-    else gemm_big_dma_kernel<true><<<grid, 512, 0, s>>>(a);
+    if (fp8) gemm_big_dma_kernel<true, true><<<grid, 512, 0, s>>>(a);
+    else gemm_big_dma_kernel<true, false><<<grid, 512, 0, s>>>(a);
   } else {
-    if (fp8) gemm_big_kernel<false, true><<<grid, 512, 0, s>>>(a);
-    else gemm_big_dma_kernel<false><<<grid, 512, 0, s>>>(a);
+    if (fp8) gemm_big_dma_kernel<false, true><<<grid, 512, 0, s>>>(a);
+    else gemm_big_dma_kernel<false, false><<<grid, 512, 0, s>>>(a);
   }
 }
 

@@ -8,9 +8,10 @@ namespace lcmoe {
 
 // Experts with 1..kSmallMaxRows routed rows run on the weight-streaming
 // (small-M) GEMM; larger ones on the LDS-tiled GEMM in M-tiles of at most
-// kBigTileRows rows.
+// kBigTileRows rows (320 = mean 256 rows per expert at the fp8 batch plus
+// its spread, so those experts stream their weights once).
 constexpr int kSmallMaxRows = 32;
-constexpr int kBigTileRows = 256;
+constexpr int kBigTileRows = 320;
 
 // Grouped GEMM tile widths (output columns per block).
 constexpr int kSmallColsGateUp = 64;   // H columns per small gate/up block

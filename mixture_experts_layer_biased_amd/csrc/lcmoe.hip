@@ -33,7 +33,9 @@ lcmoe_status check_shape(const lcmoe_shape* s) {
     return LCMOE_ERR_INVALID_ARG;
   if (s->top_k > 64 || n_experts(*s) > 2048) return LCMOE_ERR_UNSUPPORTED;
   if (s->d_model % 32 != 0 || s->d_expert % 32 != 0) return LCMOE_ERR_UNSUPPORTED;
-  if (s->w_dtype == LCMOE_W_FP8_E4M3_B128 && (s->d_model % 128 != 0 || s->d_expert % 128 != 0))
+  if (s->w_dtype == LCMOE_W_FP8_E4M3_B128 &&
+      (s->d_model % 128 != 0 || s->d_expert % 128 != 0 || s->d_model > 16384 ||
+       s->d_expert > 16384))
     return LCMOE_ERR_UNSUPPORTED;
   return LCMOE_OK;
 }
