@@ -33,18 +33,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int r = srow[k];
-      const float g = sg[k];
-      const uint4 v = r >= 0 ? *reinterpret_cast<const uint4*>(Y + (size_t)r * d + 8 * c) : xv;
-      acc[0] += g * bf16_lo(v.x);
-      acc[1] += g * bf16_hi(v.x);
-      acc[2] += g * bf16_lo(v.y);
-      acc[3] += g * bf16_hi(v.y);
-      acc[4] += g * bf16_lo(v.z);
-      acc[5] += g * bf16_hi(v.z);
-      acc[6] += g * bf16_lo(v.w);
-      acc[7] += g * bf16_hi(v.w);
+    // Four slots' rows are requested together, then added in k order.
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      uint4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = k0 + j < K ? srow[k0 + j] : -1;
+        v[j] = r >= 0 ? *reinterpret_cast<const uint4*>(Y + (size_t)r * d + 8 * c) : xv;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (k0 + j >= K) break;
+        const float g = sg[k0 + j];
+        acc[0] += g * bf16_lo(v[j].x);
+        acc[1] += g * bf16_hi(v[j].x);
+        acc[2] += g * bf16_lo(v[j].y);
+        acc[3] += g * bf16_hi(v[j].y);
+        acc[4] += g * bf16_lo(v[j].z);
+        acc[5] += g * bf16_hi(v[j].z);
+        acc[6] += g * bf16_lo(v[j].w);
+        acc[7] += g * bf16_hi(v[j].w);
+      }
     }
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);

@@ -40,14 +40,15 @@ lcmoe_status check_shape(const lcmoe_shape* s) {
   return LCMOE_OK;
 }
 
-// Router split-K factor: enough blocks to cover the chip at small T.
+// Router split-K factor: enough blocks (about two per CU) to cover the chip
+// at small T; each split keeps at least 4 k-stages of 32.
 void router_splits(int T, int E, int d, int& ks, int& kchunk) {
-  const long long base = (long long)((T + 127) / 128) * ((E + 63) / 64);
-  const int nstages = (d + 63) / 64;
-  int k = base >= 256 ? 1 : (int)std::min<long long>(16, std::max<long long>(1, 512 / std::max<long long>(base, 1)));
-  k = std::min(k, std::max(1, nstages / 2));
+  const long long base = (long long)((T + 255) / 256) * ((E + 127) / 128);
+  const int nstages = d / 32;
+  int k = (int)std::min<long long>(32, std::max<long long>(1, 512 / std::max<long long>(base, 1)));
+  k = std::min(k, std::max(1, nstages / 4));
   const int st_per = (nstages + k - 1) / k;
-  kchunk = st_per * 64;
+  kchunk = st_per * 32;
   ks = (d + kchunk - 1) / kchunk;
 }
 

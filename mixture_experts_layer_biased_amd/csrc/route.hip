@@ -20,11 +20,14 @@ namespace lcmoe {
 // (Henry, Tang & Heinecke, "Leveraging the bfloat16 Artificial Intelligence
 // Datatype for Higher-Precision Computations", ARITH 2019).
 //
-// Tile 128 tokens x 64 experts x 64 k, 4 waves (2 x 2), each wave 64 x 32
-// with v_mfma_f32_32x32x16_bf16. Global -> registers -> swizzled LDS, two
-// LDS buffers, one barrier per k stage.
+// Tile 256 tokens x 128 experts x 32 k per stage, 8 waves (2 x 4), each wave
+// 128 tokens x 32 experts: 4 x-fragments against the expert fragment's three
+// planes, 12 v_mfma_f32_32x32x16_bf16 per 16 k. The tall token side keeps the
+// 4-byte router weights' re-reads low. Global -> registers (the weights are
+// split there) -> swizzled LDS, two LDS buffers, one barrier per stage.
+// LDS rows are 64 bytes; chunk c of row r lives at c ^ ((r >> 2) & 3).
 // ---------------------------------------------------------------------------
-constexpr int RBM = 128, RBN = 64, RBK = 64;
+constexpr int RBM = 256, RBN = 128, RBK = 32;
 
 __device__ __forceinline__ void split3(float w, uint16_t& h, uint16_t& m, uint16_t& l) {
   __bf16 bh = (__bf16)w;
@@ -37,70 +40,75 @@ __device__ __forceinline__ void split3(float w, uint16_t& h, uint16_t& m, uint16
   l = *reinterpret_cast<uint16_t*>(&bl);
 }
 
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+__device__ __forceinline__ int rswz(int row, int chunk) {
+  return row * 4 + (chunk ^ ((row >> 2) & 3));
+}
+
+__global__ __launch_bounds__(512) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr,
                                                           float* __restrict__ zpart, int T,
                                                           int E, int d, int kchunk) {
-  __shared__ uint4 sA[2][RBM * 8];
-  __shared__ uint4 sB[2][3][RBN * 8];
+  __shared__ uint4 sA[2][RBM * 4];
+  __shared__ uint4 sB[2][3][RBN * 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5;
   const int t0 = blockIdx.x * RBM, e0 = blockIdx.y * RBN, sp = blockIdx.z;
   const int kbeg = sp * kchunk;
   const int kend = min(d, kbeg + kchunk);
-  const int nst = (kend - kbeg + RBK - 1) / RBK;
+  const int nst = (kend - kbeg) / RBK;  // d and kchunk are multiples of 32
 
-  uint4 ra[4];
-  float4 rb[4];
+  uint4 ra[2];
+  float4 rb[2];
   auto load_stage = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 3, c = id & 7;
-      const int t = t0 + row, k = k0 + 8 * c;
-      ra[u] = (t < T && k < kend) ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + k)
-                                  : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int id = tid + 512 * u;
+      const int row = id >> 2, c = id & 3;
+      const int t = t0 + row;
+      ra[u] = t < T ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + k0 + 8 * c)
+                    : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, q = id & 15;
-      const int e = e0 + row, k = k0 + 4 * q;
-      rb[u] = (e < E && k < kend) ? *reinterpret_cast<const float4*>(wr + (size_t)e * d + k)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < 2; ++u) {
+      const int id = tid + 512 * u;
+      const int row = id >> 3, q = id & 7;
+      const int e = e0 + row;
+      rb[u] = e < E ? *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + 4 * q)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      sA[buf][swz128(id >> 3, id & 7)] = ra[u];
+    for (int u = 0; u < 2; ++u) {
+      const int id = tid + 512 * u;
+      sA[buf][rswz(id >> 2, id & 3)] = ra[u];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, q = id & 15;
-      uint16_t h[4], m[4], l[4];
-      split3(rb[u].x, h[0], m[0], l[0]);
-      split3(rb[u].y, h[1], m[1], l[1]);
-      split3(rb[u].z, h[2], m[2], l[2]);
-      split3(rb[u].w, h[3], m[3], l[3]);
-      const int slot = swz128(row, q >> 1) * 2 + (q & 1);  // 8-byte half chunk
-      uint2* p0 = reinterpret_cast<uint2*>(sB[buf][0]);
-      uint2* p1 = reinterpret_cast<uint2*>(sB[buf][1]);
-      uint2* p2 = reinterpret_cast<uint2*>(sB[buf][2]);
-      p0[slot] = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-      p1[slot] = make_uint2(m[0] | ((uint32_t)m[1] << 16), m[2] | ((uint32_t)m[3] << 16));
-      p2[slot] = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    for (int u = 0; u < 2; ++u) {
+      const int id = tid + 512 * u;
+      const int row = id >> 3, q = id & 7;
+      uint16_t hh[4], mm[4], ll[4];
+      split3(rb[u].x, hh[0], mm[0], ll[0]);
+      split3(rb[u].y, hh[1], mm[1], ll[1]);
+      split3(rb[u].z, hh[2], mm[2], ll[2]);
+      split3(rb[u].w, hh[3], mm[3], ll[3]);
+      const int slot = rswz(row, q >> 1) * 2 + (q & 1);  // 8-byte half chunk
+      reinterpret_cast<uint2*>(sB[buf][0])[slot] =
+          make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+      reinterpret_cast<uint2*>(sB[buf][1])[slot] =
+          make_uint2(mm[0] | ((uint32_t)mm[1] << 16), mm[2] | ((uint32_t)mm[3] << 16));
+      reinterpret_cast<uint2*>(sB[buf][2])[slot] =
+          make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
     }
   };
 
-  f32x16_t acc[2];
+  f32x16_t acc[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
 
+  const int brow = 32 * wn + (lane & 31);
   load_stage(kbeg);
   store_stage(0);
   __syncthreads();
@@ -108,33 +116,34 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
     const int buf = st & 1;
     if (st + 1 < nst) load_stage(kbeg + (st + 1) * RBK);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int chunk = 2 * s + (lane >> 5);
-      const int brow = 32 * wn + (lane & 31);
-      bf16x8_t b0 = as_bf16x8(sB[buf][0][swz128(brow, chunk)]);
-      bf16x8_t b1 = as_bf16x8(sB[buf][1][swz128(brow, chunk)]);
-      bf16x8_t b2 = as_bf16x8(sB[buf][2][swz128(brow, chunk)]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 2 * ks + h;
+      const bf16x8_t b0 = as_bf16x8(sB[buf][0][rswz(brow, c)]);
+      const bf16x8_t b1 = as_bf16x8(sB[buf][1][rswz(brow, c)]);
+      const bf16x8_t b2 = as_bf16x8(sB[buf][2][rswz(brow, c)]);
+      bf16x8_t av[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int arow = 64 * wm + 32 * i + (lane & 31);
-        bf16x8_t a = as_bf16x8(sA[buf][swz128(arow, chunk)]);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b2, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        av[i] = as_bf16x8(sA[buf][rswz(128 * wm + 32 * i + (lane & 31), c)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], b2, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], b1, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], b0, acc[i], 0, 0, 0);
       }
     }
     if (st + 1 < nst) store_stage(buf ^ 1);
     __syncthreads();
   }
 
-  const int e = e0 + 32 * wn + (lane & 31);
+  const int e = e0 + brow;
   if (e < E) {
     float* zp = zpart + (size_t)sp * T * E;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int t = t0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int t = t0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (t < T) zp[(size_t)t * E + e] = acc[i][v];
       }
   }
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
 void launch_router(const uint16_t* x, const float* wr, float* zpart, int T, int E, int d,
                    int ks, int kchunk, hipStream_t s) {
   dim3 grid((T + RBM - 1) / RBM, (E + RBN - 1) / RBN, ks);
-  router_gemm_kernel<<<grid, 256, 0, s>>>(x, wr, zpart, T, E, d, kchunk);
+  router_gemm_kernel<<<grid, 512, 0, s>>>(x, wr, zpart, T, E, d, kchunk);
 }
 
 void launch_topk(const float* zpart, int ks, const float* bias, int T, int E, int K, int* idx,
