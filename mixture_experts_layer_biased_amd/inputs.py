@@ -60,6 +60,10 @@ CONFIGS = {
     # followed by 20 bias-update steps (mu=1e-3, K_e=8) on fresh batches.
     "fp8": LayerConfig("fp8", 6144, 512, 256, 12, 2048, 16384, seed=5, wdtype="fp8",
                        extra=dict(bias_steps=20, mu=1e-3, k_e=8.0)),
+    # LongCat shape, bf16, T=32768 (about 512 rows per FFN expert): the batch
+    # at which the bf16 grouped GEMM has more MFMA work than weight bytes
+    # (512 FLOP/B). An extra measurement point, not one of the five above.
+    "prefill32k": LayerConfig("prefill32k", 6144, 512, 256, 12, 2048, 32768, seed=6),
 }
 
 
