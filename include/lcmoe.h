@@ -41,8 +41,9 @@
  *                          N < 1, Z < 0, bad dtype code, mu/k_e not finite.
  *   LCMOE_ERR_UNSUPPORTED  K > 64, N+Z > 2048, d % 32 != 0, I % 32 != 0,
  *                          fp8 with d % 128 or I % 128 != 0 or d or I
- *                          above 16384, a tensor
- *                          pointer not 16-byte aligned, T*K >= 2^31.
+ *                          above 16384, one expert's W13 of 4 GiB or
+ *                          more, a tensor pointer not 16-byte aligned,
+ *                          T*K >= 2^31, (forward) x of 4 GiB or more.
  *   LCMOE_ERR_WORKSPACE    ws is NULL or ws_bytes too small.
  *   LCMOE_ERR_HIP          a HIP launch failed (hipGetLastError).
  */

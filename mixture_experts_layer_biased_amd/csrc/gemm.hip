@@ -196,32 +196,37 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 // large-M kernel: direct-to-LDS pipeline (bf16 or fp8 weights)
 //
 // Tile up to 320 token rows x 256 weight rows; the k loop runs in stages of
-// 32. Both operands move HBM -> LDS with global_load_lds_dwordx4 (no
+// 64. Both operands move HBM -> LDS with global_load_lds_dwordx4 (no
 // register staging) into a ring of LDS slots, all but one in flight while
-// one is multiplied. fp8 codes stay one byte in LDS and become
-// bf16(fl32(q) * s) in registers after the LDS read. The token rows form ten 32-row fragments,
-// fragment i belonging to wave row i & 1, so any row count splits evenly
-// over the two waves that share a SIMD.
+// one is multiplied. A stage moves a whole 128-byte line of every x row and
+// bf16 weight row (eight lanes per row, eight rows per copy instruction):
+// the L1/L2 request rate, not the byte rate, bounds these copies, so whole
+// lines carry twice the bytes of 64-byte half-line requests. fp8 codes stay
+// one byte in LDS (64 bytes per weight row per stage) and become
+// bf16(fl32(q) * s) in registers after the LDS read. The token rows form ten
+// 32-row fragments, fragment i belonging to wave row i & 1, so any row count
+// splits evenly over the two waves that share a SIMD.
 //
 // LDS layouts (16-byte chunks; gfx950 LDS has 64 banks, so each group of 16
 // lanes must touch 16 distinct 16-byte slots of a 256-byte window):
-//   x tile and bf16 weight tile: 64-byte rows, chunk c of row r at
-//     c ^ ((r >> 2) & 3);
-//   fp8 weight tile: 32-byte rows, chunk c of row r at c ^ ((r >> 3) & 1).
+//   x tile and bf16 weight tile: 128-byte rows, chunk c of row r at
+//     c ^ ((r >> 1) & 7);
+//   fp8 weight tile: 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3).
 // One copy instruction fills a contiguous 1 KB block: lane l writes the
 // block's l-th chunk, so it loads the logical chunk the swizzle puts there.
 //
-// k order inside a 32-wide stage (the same for both operands, as the MFMA
-// requires): bf16 weights: k-step ks and lane half h take k = 16 ks + 8 h
-// + [0, 8) (operand chunk 2 ks + h); fp8 weights: k = 16 h + 8 ks + [0, 8)
-// (x chunk 2 h + ks), so one 16-byte read of weight chunk h gives lane half
-// h its 16 codes for both k-steps.
+// k order inside a 64-wide stage (the same for both operands, as the MFMA
+// requires), for half kk (0, 1), k-step j (0, 1) and lane half h: bf16
+// weights: k = 32 kk + 16 j + 8 h + [0, 8) (operand chunk 4 kk + 2 j + h);
+// fp8 weights: k = 32 kk + 16 h + 8 j + [0, 8) (x chunk 4 kk + 2 h + j), so
+// one 16-byte read of weight chunk 2 kk + h gives lane half h its 16 codes
+// for both k-steps of the half.
 //
 // Each wave waits for its own copies of a stage (s_waitcnt vmcnt with the
 // count of its younger copies still allowed in flight) and a raw s_barrier
 // then publishes the stage; no fence, which would drain the pipeline.
 // ===========================================================================
-constexpr int DBK = 32;  // k per pipeline stage
+constexpr int DBK = 64;  // k per pipeline stage
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -270,34 +275,36 @@ __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// One global_load_lds_dwordx4: lane l copies 16 bytes from g into LDS at
-// lds + 16*l. Issued as inline asm so the compiler does not track it: every
-// wait on these copies is the explicit wait_vmcnt above. M0 (the LDS base of
-// the copy) is written here and used by nothing else in these kernels.
-__device__ __forceinline__ void dma16(const void* g, const uint4* lds) {
+// One global_load_lds_dwordx4 in its scalar-base form: lane l copies 16
+// bytes from sbase + voff (voff a 32-bit unsigned per-lane byte offset, sbase
+// wave-uniform) into LDS at lds + 16*l. Issued as inline asm so the compiler
+// does not track it: every wait on these copies is the explicit wait_vmcnt
+// above. M0 (the LDS base of the copy) is written here and used by nothing
+// else in these kernels.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, const uint4* lds) {
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(l) : "memory");
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(bs), "s"(l) : "memory");
 }
-// 64-byte LDS rows: chunk c of row r lives at c ^ ((r >> 2) & 3).
+// 64-byte LDS rows (fp8 weight tile): chunk c of row r lives at c ^ ((r >> 2) & 3).
 __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * 4 + (chunk ^ ((row >> 2) & 3));
 }
-// 32-byte LDS rows (fp8 weight tile): chunk c of row r at c ^ ((r >> 3) & 1).
-__device__ __forceinline__ int swz32(int row, int chunk) {
-  return row * 2 + (chunk ^ ((row >> 3) & 1));
-}
 
 // The ring lives in one 144 KB LDS array. A slot holds the x rows of the
-// tile (16-row groups, 64 B per row) followed by the weight tile; the slot
-// count is what fits for the tile's actual row count, capped at 4 (bf16) or
-// 5 (fp8) stages.
+// tile (8-row groups, 128 B per row) followed by the weight tile; the slot
+// count is what fits for the tile's actual row count, capped at 3.
 template <bool FP8>
 struct DmaTile {
-  static constexpr int LDS_CHUNKS = 9216;                  // 144 KB
-  static constexpr int MAX_SLOTS = FP8 ? 5 : 4;  // deeper rings measured no faster
-  static constexpr int B_CHUNKS = FP8 ? 256 * 2 : 256 * 4; // weight tile, 8 or 16 KB
-  static constexpr int AGROUPS = kBigTileRows / 16;        // 16-row copy groups of the x tile
+  static constexpr int LDS_CHUNKS = 9216;                   // 144 KB
+  static constexpr int MAX_SLOTS = 3;
+  static constexpr int B_CHUNKS = FP8 ? 256 * 4 : 256 * 8;  // weight tile, 16 or 32 KB
+  static constexpr int AGROUPS = kBigTileRows / 8;          // 8-row copy groups of the x tile
+  static constexpr int AG_PER_WAVE = AGROUPS / 8;           // 5
+  static constexpr int BG_PER_WAVE = FP8 ? 2 : 4;           // weight copies per wave
 };
 
 template <bool GATEUP, bool FP8>
@@ -343,64 +350,80 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
     }
   };
 
-  // Copy assignment. x tile: wave w fills row groups w, w+8, w+16 (16 rows,
-  // 1 KB each). bf16 weights: groups w and w+8; fp8 weights: group w of 32
-  // rows (1 KB). Groups wholly outside the valid rows are skipped.
-  const uint16_t* asrc[3];
-  const char* bsrc[2];
-  bool ause[3], buse[2];
+  // Copy assignment. x tile: wave w fills 8-row groups w + 8 g (1 KB each,
+  // eight lanes per row). bf16 weights: 8-row groups w + 8 g; fp8 weights:
+  // 16-row groups w + 8 g (64 B per row, four lanes per row). Groups wholly
+  // outside the valid rows are skipped. When kdim is an odd multiple of 32
+  // the last stage holds only the first 32 k of each row: lanes past the end
+  // of a row then load that row's chunk c - 4, which no MFMA reads.
+  //
+  // Byte offsets of each lane's copies from the operand bases (all of x, the
+  // tile's first H row, or this expert's weight matrix; below 4 GiB, which
+  // the host checks); the k position goes into the scalar base.
+  uint32_t aoff[TL::AG_PER_WAVE], boff[TL::BG_PER_WAVE];
+  bool ause[TL::AG_PER_WAVE], buse[TL::BG_PER_WAVE];
+  const int esz = FP8 ? 1 : 2;  // weight bytes per element
+  const char* wexp = static_cast<const char*>(a.w) + (size_t)e * a.rows_total * kdim * esz;
+  const char* abase = reinterpret_cast<const char*>(a.src) + (GATEUP ? 0 : (size_t)rowbase * kdim * 2);
+  // Logical chunk loaded by this lane into an 8-row group g (row 8 g + (lane >> 3)):
+  // (row >> 1) & 7 = (4 g + (lane >> 4)) & 7 depends on g only through g & 1,
+  // which is wave & 1 for every group g = wave + 8 g2 of this wave.
+  const int ac = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
 #pragma unroll
-  for (int g2 = 0; g2 < 3; ++g2) {
+  for (int g2 = 0; g2 < TL::AG_PER_WAVE; ++g2) {
     const int g = wave + 8 * g2;
-    const int row = 16 * g + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
-    ause[g2] = g < TL::AGROUPS && 16 * g < rows;
+    const int row = 8 * g + (lane >> 3);
+    ause[g2] = 8 * g < rows;
     const int rr = row < rows ? row : 0;
-    if (GATEUP)
-      asrc[g2] = a.src + (size_t)(a.perm[rowbase + rr] / a.topk) * kdim + 8 * c;
-    else
-      asrc[g2] = a.src + (size_t)(rowbase + rr) * kdim + 8 * c;
+    const size_t srow = GATEUP ? (size_t)(a.perm[rowbase + rr] / a.topk) : (size_t)rr;
+    aoff[g2] = (uint32_t)(srow * kdim * 2 + 16 * ac);
   }
   if (FP8) {
-    const int row = 32 * wave + (lane >> 1);
-    const int c = (lane & 1) ^ ((row >> 3) & 1);
-    const int wr = wrow_of(row);
-    buse[0] = wrow_of(32 * wave) >= 0;
-    buse[1] = false;
-    bsrc[0] = static_cast<const char*>(a.w) + ((size_t)e * a.rows_total + (wr >= 0 ? wr : 0)) * kdim + 16 * c;
-    bsrc[1] = bsrc[0];
-  } else {
 #pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
+    for (int g2 = 0; g2 < TL::BG_PER_WAVE; ++g2) {
       const int g = wave + 8 * g2;
       const int row = 16 * g + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
       const int wr = wrow_of(row);
       buse[g2] = wrow_of(16 * g) >= 0;
-      bsrc[g2] = static_cast<const char*>(a.w) +
-                 (((size_t)e * a.rows_total + (wr >= 0 ? wr : 0)) * kdim + 8 * c) * 2;
+      boff[g2] = (uint32_t)((size_t)(wr >= 0 ? wr : 0) * kdim + 16 * c);
+    }
+  } else {
+#pragma unroll
+    for (int g2 = 0; g2 < TL::BG_PER_WAVE; ++g2) {
+      const int g = wave + 8 * g2;
+      const int row = 8 * g + (lane >> 3);
+      const int wr = wrow_of(row);
+      buse[g2] = wrow_of(8 * g) >= 0;
+      boff[g2] = (uint32_t)(((size_t)(wr >= 0 ? wr : 0) * kdim + 8 * ac) * 2);
     }
   }
-  const int per_stage =
-      (int)ause[0] + (int)ause[1] + (int)ause[2] + (int)buse[0] + (int)buse[1];
-  const int nst = kdim / DBK;
+  int per_stage = 0;
+#pragma unroll
+  for (int g2 = 0; g2 < TL::AG_PER_WAVE; ++g2) per_stage += (int)ause[g2];
+#pragma unroll
+  for (int g2 = 0; g2 < TL::BG_PER_WAVE; ++g2) per_stage += (int)buse[g2];
+  const int nst = (kdim + DBK - 1) / DBK;
+  const bool half_tail = (kdim % DBK) != 0;  // last stage holds 32 k
   // Ring geometry for this tile (wave-uniform).
-  const int a_chunks = ((rows + 15) >> 4) * 64;
+  const int a_chunks = ((rows + 7) >> 3) * 64;
   const int slot = a_chunks + TL::B_CHUNKS;
   const int nslots = min(TL::MAX_SLOTS, TL::LDS_CHUNKS / slot);
 
   auto issue = [&](int s) {
     const int k0 = s * DBK;
+    const char* xs = abase + 2 * (size_t)k0;
+    const char* ws = wexp + (size_t)k0 * esz;
+    // Tail stage of an odd multiple of 32 (bf16 only): chunks 4..7 of a row
+    // do not exist; those lanes load chunk c - 4 (64 bytes back) instead.
+    const uint32_t back = (half_tail && s == nst - 1 && ac >= 4) ? 64u : 0u;
     const uint4* base = lds + (s % nslots) * slot;
-    if (ause[0]) dma16(asrc[0] + k0, base + wave * 64);
-    if (ause[1]) dma16(asrc[1] + k0, base + (wave + 8) * 64);
-    if (ause[2]) dma16(asrc[2] + k0, base + (wave + 16) * 64);
-    if (FP8) {
-      if (buse[0]) dma16(bsrc[0] + k0, base + a_chunks + wave * 64);
-    } else {
-      if (buse[0]) dma16(bsrc[0] + 2 * k0, base + a_chunks + wave * 64);
-      if (buse[1]) dma16(bsrc[1] + 2 * k0, base + a_chunks + (wave + 8) * 64);
-    }
+#pragma unroll
+    for (int g2 = 0; g2 < TL::AG_PER_WAVE; ++g2)
+      if (ause[g2]) dma16(xs, aoff[g2] - back, base + (wave + 8 * g2) * 64);
+#pragma unroll
+    for (int g2 = 0; g2 < TL::BG_PER_WAVE; ++g2)
+      if (buse[g2]) dma16(ws, boff[g2] - (FP8 ? 0u : back), base + a_chunks + (wave + 8 * g2) * 64);
   };
 
   constexpr int MF = kBigTileRows / 64;  // fragments per wave (5)
@@ -440,15 +463,15 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
   const int nact = __builtin_amdgcn_readfirstlane(
       max(0, min(MF, (rows - 32 * wm + 63) / 64)));
 
-  // Multiply one stage: all LDS operand reads first, then the MFMAs.
-  auto compute_n = [&](auto NA_c, int s) {
+  // Multiply half kk of one stage: all LDS operand reads first, then the MFMAs.
+  auto compute_half = [&](auto NA_c, int s, int kk) {
     constexpr int NA = decltype(NA_c)::value;
     const uint4* A = lds + (s % nslots) * slot;
     const uint4* B = A + a_chunks;
     bf16x8_t Bv[2][2], Av[2][NA > 0 ? NA : 1];
     if (FP8) {
-      const uint4 q0 = B[swz32(brow0, h)];
-      const uint4 q1 = B[swz32(brow1, h)];
+      const uint4 q0 = B[swz64(brow0, 2 * kk + h)];
+      const uint4 q1 = B[swz64(brow1, 2 * kk + h)];
       const int kb = (s * DBK) >> 7;
       const float s0 = __int_as_float(__builtin_amdgcn_readlane(scv[0][kb >> 6], kb & 63));
       const float s1 = __int_as_float(__builtin_amdgcn_readlane(scv[1][kb >> 6], kb & 63));
@@ -458,24 +481,24 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
       Bv[1][1] = as_bf16x8(fp8x8_scaled_to_bf16x8(q1.z, q1.w, s1));
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Bv[ks][0] = as_bf16x8(B[swz64(brow0, 2 * ks + h)]);
-        Bv[ks][1] = as_bf16x8(B[swz64(brow1, 2 * ks + h)]);
+      for (int j = 0; j < 2; ++j) {
+        Bv[j][0] = as_bf16x8(B[swz128(brow0, 4 * kk + 2 * j + h)]);
+        Bv[j][1] = as_bf16x8(B[swz128(brow1, 4 * kk + 2 * j + h)]);
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = FP8 ? 2 * h + ks : 2 * ks + h;
+    for (int j = 0; j < 2; ++j) {
+      const int c = FP8 ? 4 * kk + 2 * h + j : 4 * kk + 2 * j + h;
 #pragma unroll
       for (int i = 0; i < NA; ++i)
-        Av[ks][i] = as_bf16x8(A[swz64(frow(i) + (lane & 31), c)]);
+        Av[j][i] = as_bf16x8(A[swz128(frow(i) + (lane & 31), c)]);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[ks][i], Bv[ks][0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[ks][i], Bv[ks][1], acc[i][1], 0, 0, 0);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[j][i], Bv[j][0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[j][i], Bv[j][1], acc[i][1], 0, 0, 0);
       }
   };
   // Stage s: wait for its copies (younger stages stay in flight), publish,
@@ -487,7 +510,8 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
       wait_vmcnt_upto(per_stage * min(nslots - 2, nst - 1 - s));
       raw_barrier();
       if (s + nslots - 1 < nst) issue(s + nslots - 1);
-      compute_n(NA_c, s);
+      compute_half(NA_c, s, 0);
+      if (!(half_tail && s == nst - 1)) compute_half(NA_c, s, 1);
     }
   };
   switch (nact) {

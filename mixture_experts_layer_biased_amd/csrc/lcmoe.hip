@@ -33,6 +33,9 @@ lcmoe_status check_shape(const lcmoe_shape* s) {
     return LCMOE_ERR_INVALID_ARG;
   if (s->top_k > 64 || n_experts(*s) > 2048) return LCMOE_ERR_UNSUPPORTED;
   if (s->d_model % 32 != 0 || s->d_expert % 32 != 0) return LCMOE_ERR_UNSUPPORTED;
+  // One expert's gate/up matrix is addressed with 32-bit byte offsets.
+  const long long wbytes = s->w_dtype == LCMOE_W_FP8_E4M3_B128 ? 1 : 2;
+  if (2ll * s->d_expert * s->d_model * wbytes >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
   if (s->w_dtype == LCMOE_W_FP8_E4M3_B128 &&
       (s->d_model % 128 != 0 || s->d_expert % 128 != 0 || s->d_model > 16384 ||
        s->d_expert > 16384))
@@ -212,6 +215,8 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
     return LCMOE_ERR_INVALID_ARG;
   if (T > 0 && fp8 && (w13_scale == nullptr || w2_scale == nullptr)) return LCMOE_ERR_INVALID_ARG;
   if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
+  // x rows are gathered with 32-bit byte offsets.
+  if ((long long)T * shape->d_model * 2 >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
   if (T == 0) {
     if (hipMemsetAsync(counts, 0, (size_t)n_experts(*shape) * 4, stream) != hipSuccess)
       return LCMOE_ERR_HIP;

@@ -79,6 +79,7 @@ def shp(**kw):
     (dict(d_model=48), ERR_UNSUPPORTED),
     (dict(d_expert=40), ERR_UNSUPPORTED),
     (dict(w_dtype=1), ERR_UNSUPPORTED),            # fp8 needs d, I % 128 == 0
+    (dict(d_model=32768, d_expert=32768), ERR_UNSUPPORTED),  # one W13 of 4 GiB
 ])
 def test_invalid_shapes(kw, status):
     assert _route(shp(**kw), 4) == status
@@ -109,6 +110,8 @@ def test_invalid_arguments_forward_and_bias():
     assert _forward(s, 4, ws=FAKE, wsb=1024) == ERR_WORKSPACE
     f = make_shape(128, 8, 4, 3, 128, 1)
     assert _forward(f, 4) == ERR_INVALID_ARG        # fp8 without scales
+    wide = make_shape(8192, 8, 4, 3, 32)
+    assert _forward(wide, 2 ** 18) == ERR_UNSUPPORTED  # x of 4 GiB (32-bit gather offsets)
     L = lcmoe.lib()
     assert L.lcmoe_bias_update(ctypes.byref(s), 0, FAKE, 1e-3, 2.0, FAKE, None) == ERR_INVALID_ARG
     assert L.lcmoe_bias_update(ctypes.byref(s), 16, None, 1e-3, 2.0, FAKE, None) == ERR_INVALID_ARG

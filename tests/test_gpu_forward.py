@@ -58,6 +58,18 @@ def test_forward_all_tokens(name, T):
     check_rows(cfg, L, x, res, np.arange(T), cache={})
 
 
+@pytest.mark.parametrize("d,inter,T", [(96, 160, 1500), (160, 96, 1500), (1056, 544, 700)])
+def test_forward_k_odd_multiple_of_32(d, inter, T):
+    # d or I an odd multiple of 32: the large-M kernel's last k stage holds
+    # 32 of its 64 k; T puts 2 M-tiles on some experts (tiny) or one (1056).
+    cfg, L = layer("tiny", d=d, inter=inter)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    res = run_forward(cfg, L, x)
+    counts = res["counts"].cpu().numpy()[: cfg.n_ffn]
+    assert counts.max() > 32
+    check_rows(cfg, L, x, res, np.arange(T), cache={})
+
+
 def _sample(x, n, extra_large=0):
     T = x.shape[0]
     toks = list(np.linspace(0, T - 1, n).astype(int))
