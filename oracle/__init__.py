@@ -7,8 +7,10 @@ never does, and the two share no code.
 
 Source of what is computed: "LongCat-Flash" (llm-wiki entity page), section
 2.1 "Zero-Computation Experts" (the MoE sum, the zero-expert identity, the
-expert-bias update and its symbols), section 2.3.2 (softmax gating), and the
-model table in section 1 "核心参数" (layer shape).
+expert-bias update and its symbols, and the device-level load-balance loss
+with the zero experts as one extra group), section 2.3.2 (softmax gating), the
+training-stability section (hidden z-loss), and the model table in section 1
+"核心参数" (layer shape).
 """
 
 from .lcmoe_oracle import (  # noqa: F401
@@ -28,4 +30,7 @@ from .lcmoe_oracle import (  # noqa: F401
     forward,
     dense_masked_forward,
     bias_update,
+    expert_groups,
+    load_balance_stats,
+    hidden_z_loss,
 )

@@ -20,6 +20,16 @@ Every function follows a passage of the "LongCat-Flash" llm-wiki entity page
            the fp32 bias.
   R-fp8    fp8 weights are OCP E4M3FN codes with one fp32 scale per 128x128
            block; the dequantised weight is fl32(q * s).
+  R-grp    for the device-level balance statistic the N FFN experts form D
+           groups of N/D consecutive experts (the placement of expert
+           parallelism over D devices); the Z zero experts are group D+1.
+  R-lb     P_j is the mean over tokens of the softmax mass (all N+Z unbiased
+           logits) in group j; f_j is group j's share of the T*K selected
+           slots divided by its target share, K_e/(K*D) for each FFN group
+           and (K-K_e)/K for the zero group, so routing at the target ratio
+           K_e : (K-K_e), even over the FFN groups, has f_j = 1 everywhere.
+  R-zl     the hidden z-loss is taken over the layer input hidden states,
+           i running over d_model.
 
 Precision: all arithmetic on activations is fp64 except where a step is
 defined in fp32 (the selection score, the fp8 dequantised weight, the bias
@@ -287,3 +297,62 @@ def bias_update(bias, counts, n_ffn, k, mu, k_e, t_all):
         delta = (float(mu) * num) / den
         b[i] = np.float32(float(b[i]) + delta)
     return b
+
+
+# ----------------------------------------------------------------------------
+# Router-side statistics (forward values of the training-side terms)
+# ----------------------------------------------------------------------------
+
+
+def expert_groups(n_ffn, n_zero, n_groups):
+    """Group of every expert (reading R-grp): FFN expert i is in group
+    i // (n_ffn / n_groups); every zero-computation expert is in group
+    n_groups (the page's group D+1, counted from 0 here)."""
+    if n_groups < 1 or n_ffn % n_groups:
+        raise ValueError("n_groups must divide n_ffn")
+    gs = n_ffn // n_groups
+    return np.array([i // gs for i in range(n_ffn)] + [n_groups] * n_zero, dtype=np.int64)
+
+
+def load_balance_stats(z, counts, n_ffn, n_zero, k, n_groups, k_e, alpha):
+    """Device-level load-balance loss with the zero experts as one extra
+    group ("LongCat-Flash" section 2.1, load-balance control: L_LB = alpha *
+    sum over the D+1 groups of f_j * P_j; the zero group drives the FFN to
+    zero ratio toward K_e : (K - K_e)), under readings R-grp and R-lb.
+
+    z: [T, E] router logits (unbiased); counts: [E] tokens per expert.
+    Returns (L_LB, f[D+1], P[D+1]); T = 0 gives zeros.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    counts = np.asarray(counts, dtype=np.int64)
+    T, E = z.shape
+    D = n_groups
+    grp = expert_groups(n_ffn, n_zero, D)
+    f = np.zeros(D + 1)
+    P = np.zeros(D + 1)
+    if T == 0:
+        return 0.0, f, P
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    p = e / e.sum(axis=1, keepdims=True)          # softmax over all N+Z experts
+    target = np.array([k_e / (k * D)] * D + [(k - k_e) / k])
+    for j in range(D + 1):
+        P[j] = p[:, grp == j].sum(axis=1).mean()
+        share = counts[grp == j].sum() / (T * k)  # share of the T*K selected slots
+        # K_e = K sets no target for the zero group; its term is then 0.
+        f[j] = share / target[j] if target[j] > 0 else 0.0
+    return float(alpha * np.sum(f * P)), f, P
+
+
+def hidden_z_loss(h, lam):
+    """Hidden z-loss ("LongCat-Flash" section on training stability,
+    activation stability: L_Z = (lambda / T) * sum_t (log sum_i exp|h_t^i|)^2),
+    over the layer input hidden states h [T, d] (reading R-zl). The
+    log-sum-exp is taken with its maximum factored out. T = 0 gives 0."""
+    h = np.abs(np.asarray(h, dtype=np.float64))
+    T = h.shape[0]
+    if T == 0:
+        return 0.0
+    mx = h.max(axis=1)
+    lse = mx + np.log(np.exp(h - mx[:, None]).sum(axis=1))
+    return float(lam / T * np.sum(lse * lse))

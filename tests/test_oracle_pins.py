@@ -397,3 +397,97 @@ def test_page_shape_supports_gated_expert_and_k_e_8():
     # mean activation implies ~8 FFN experts per token = K*N/E (symmetric point)
     k_e_mean = (act["mean"] - act["min"]) / per_slot_b
     assert math.isclose(k_e_mean, K * N / (N + Z), rel_tol=0.01)
+
+
+# ----------------------------------------------------------------------------
+# Router-side statistics: device-level balance loss with the zero group, and
+# the hidden z-loss ("LongCat-Flash" section 2.1 load-balance control; the
+# training-stability section, activation stability).
+# ----------------------------------------------------------------------------
+
+
+def _random_counts(rng, T, K, E):
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    return np.bincount(idx.ravel(), minlength=E)
+
+
+@pytest.mark.parametrize("N,Z,D", [(8, 4, 2), (8, 4, 8), (64, 32, 8), (16, 0, 4)])
+def test_balance_stats_uniform_logits(N, Z, D):
+    # z = 0: every expert has probability 1/E, so P_j = |G_j| / E.
+    E, K, T = N + Z, 3, 5
+    rng = np.random.default_rng(1)
+    counts = _random_counts(rng, T, K, E)
+    _, _, P = oracle.load_balance_stats(np.zeros((T, E)), counts, N, Z, K, D, 2.0, 1.0)
+    want = np.array([N / D / E] * D + [Z / E])
+    assert np.allclose(P, want, rtol=0, atol=1e-15)
+
+
+def test_balance_stats_target_routing_has_unit_f():
+    # N=8, Z=4, K=3, K_e=2, D=2, T=4: 12 slots, targets 1/3 per FFN group and
+    # 1/3 for the zero group, i.e. 4 slots each -> f = 1 for all three groups,
+    # so L_LB = alpha * sum_j P_j = alpha for any logits.
+    N, Z, K, D, T = 8, 4, 3, 2, 4
+    counts = np.array([1, 1, 2, 0, 0, 3, 1, 0, 2, 0, 1, 1])
+    rng = np.random.default_rng(2)
+    z = rng.normal(size=(T, N + Z)) * 3
+    L, f, P = oracle.load_balance_stats(z, counts, N, Z, K, D, 2.0, 0.25)
+    assert np.allclose(f, 1.0, rtol=0, atol=1e-15)
+    assert math.isclose(P.sum(), 1.0, rel_tol=1e-14)
+    assert math.isclose(L, 0.25, rel_tol=1e-14)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_balance_stats_shares_and_shift_invariance(seed):
+    N, Z, K, D, T, k_e = 64, 32, 6, 8, 50, 4.0
+    rng = np.random.default_rng(seed)
+    z = rng.normal(size=(T, N + Z))
+    counts = _random_counts(rng, T, K, N + Z)
+    L, f, P = oracle.load_balance_stats(z, counts, N, Z, K, D, k_e, 1.0)
+    target = np.array([k_e / (K * D)] * D + [(K - k_e) / K])
+    assert math.isclose(float(np.sum(f * target)), 1.0, rel_tol=1e-13)  # shares sum to 1
+    # softmax is invariant to a per-token shift of the logits
+    L2, f2, P2 = oracle.load_balance_stats(z + rng.normal(size=(T, 1)) * 40, counts, N, Z, K, D,
+                                           k_e, 1.0)
+    assert np.allclose(P2, P, rtol=1e-12, atol=0) and np.array_equal(f2, f)
+    # relabelling experts inside one group changes nothing
+    perm = np.arange(N + Z)
+    perm[:N // D] = perm[:N // D][::-1]
+    L3, _, P3 = oracle.load_balance_stats(z[:, perm], counts[perm], N, Z, K, D, k_e, 1.0)
+    assert np.allclose(P3, P, rtol=1e-13) and math.isclose(L3, L, rel_tol=1e-13)
+
+
+def test_balance_stats_reduce_to_switch_style_loss():
+    # One expert per group, no zero experts, K_e = K: f_i = N * c_i / (T K)
+    # and P_i = mean softmax probability -- the familiar per-expert auxiliary
+    # balance loss, evaluated here with torch's softmax.
+    N, K, T = 16, 4, 40
+    rng = np.random.default_rng(5)
+    z = rng.normal(size=(T, N)) * 2
+    counts = _random_counts(rng, T, K, N)
+    L, f, P = oracle.load_balance_stats(z, counts, N, 0, K, N, float(K), 0.5)
+    Pt = torch.softmax(torch.tensor(z, dtype=torch.float64), dim=1).mean(0).numpy()
+    ft = N * counts / (T * K)
+    assert np.allclose(P[:N], Pt, rtol=1e-13) and np.allclose(f[:N], ft, rtol=1e-14)
+    assert f[N] == 0.0 and P[N] == 0.0
+    assert math.isclose(L, 0.5 * float(np.sum(ft * Pt)), rel_tol=1e-13)
+
+
+def test_hidden_z_loss_closed_forms():
+    d, lam = 6144, 1e-3
+    assert math.isclose(oracle.hidden_z_loss(np.zeros((3, d)), lam), lam * math.log(d) ** 2,
+                        rel_tol=1e-14)
+    c = -2.5  # |h| = 2.5 everywhere
+    assert math.isclose(oracle.hidden_z_loss(np.full((2, d), c), lam),
+                        lam * (2.5 + math.log(d)) ** 2, rel_tol=1e-14)
+    # one large entry: lse = 80 + log(1 + (d - 1) e^-80) = 80 to double precision
+    h = np.zeros((1, d))
+    h[0, 17] = -80.0
+    assert math.isclose(oracle.hidden_z_loss(h, 1.0), 80.0 ** 2, rel_tol=1e-15)
+    # against torch.logsumexp on random states (sign-symmetric in h)
+    rng = np.random.default_rng(3)
+    h = rng.normal(size=(7, 333)) * 3
+    lse = torch.logsumexp(torch.tensor(np.abs(h)), dim=1).numpy()
+    want = 0.3 / 7 * float(np.sum(lse ** 2))
+    assert math.isclose(oracle.hidden_z_loss(h, 0.3), want, rel_tol=1e-13)
+    assert math.isclose(oracle.hidden_z_loss(-h, 0.3), want, rel_tol=1e-13)
+    assert oracle.hidden_z_loss(np.zeros((0, 4)), 1.0) == 0.0
