@@ -284,6 +284,28 @@ def measure(cfg, steps, warmup, hip):
         layer=dict(algorithmic_bytes=lb, hbm_frac=lb / (ms / 1e3) / PEAK_HBM,
                    mfma_frac=gemm_flops / (ms / 1e3) / PEAK_BF16),
     )
+    # Router-side statistics (outside the layer step): one routing call that
+    # exports the logits, then lcmoe_router_stats timed on its own.
+    r = lcmoe.route(shape, x, L["w_router"], L["bias"], ws=ws, logits=True)
+    D = 8 if cfg.n_ffn % 8 == 0 else 1
+    k_e = cfg.k * cfg.n_ffn / cfg.n_experts
+    sws = torch.empty(lcmoe.router_stats_workspace_bytes(shape, D), dtype=torch.uint8,
+                      device="cuda")
+    lcmoe.router_stats(shape, x, r["logits"], r["counts"], D, k_e, ws=sws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    a.record()
+    for _ in range(reps):
+        lcmoe.router_stats(shape, x, r["logits"], r["counts"], D, k_e, ws=sws)
+    b.record()
+    torch.cuda.synchronize()
+    st_ms = a.elapsed_time(b) / reps
+    st_bytes = T * cfg.n_experts * 4 + T * cfg.d * 2
+    res["router_stats"] = dict(ms=st_ms, groups=D, algorithmic_bytes=st_bytes,
+                               hbm_frac=st_bytes / (st_ms / 1e3) / PEAK_HBM)
+    del r, sws
     return res, (L, x, out)
 
 
@@ -387,8 +409,8 @@ def main():
         results[name] = res
         print(f"[bench] {name}: {res['ms_per_step']:.3f} ms/step, "
               f"{res['tokens_per_s']:.0f} tok/s, dominant {res['dominant_kernel']} "
-              f"{res['roofline']['frac']:.3f} of {res['roofline']['bound']}", file=sys.stderr,
-              flush=True)
+              f"{res['roofline']['frac']:.3f} of {res['roofline']['bound']}; router stats "
+              f"{res['router_stats']['ms']:.3f} ms", file=sys.stderr, flush=True)
         if name == names[0] and not args.no_cpu_baseline:
             baseline = cpu_baseline(cfg, keep[0], keep[1], keep[2], args.cpu_experts)
         del keep

@@ -199,6 +199,45 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
                                const int32_t* counts, double mu, double k_e,
                                float* bias, hipStream_t stream);
 
+/* Router-side statistics ("LongCat-Flash" section 2.1, load-balance control:
+ * the device-level load-balance loss L_LB = alpha * sum_{j=1..D+1} f_j P_j
+ * with the zero-computation experts as group D+1; the training-stability
+ * section, activation stability: the hidden z-loss
+ * L_Z = lambda/T * sum_t (log sum_i exp|h_t^i|)^2). Forward values only; no
+ * gradients. Definitions where the page is silent:
+ *   groups  FFN expert i is in group i / (N/D) (D consecutive blocks, the
+ *           placement of expert parallelism over D devices); every zero
+ *           expert is in group D+1.
+ *   P_j     mean over the T tokens of the softmax mass of group j, softmax
+ *           over all N+Z unbiased logits.
+ *   f_j     group j's share of the T*K selected slots (from counts) divided
+ *           by its target share: K_e/(K*D) for each FFN group, (K-K_e)/K for
+ *           the zero group (K_e = K sets no zero-group target: f = 0). Routing
+ *           at the target ratio K_e : (K-K_e), even over the FFN groups,
+ *           gives f_j = 1 for every group.
+ *   h_t     the layer input x_t (i runs over d_model).
+ * Deterministic: fixed summation orders (per-token values in fp32, sums over
+ * tokens and groups in fp64), no atomics. T = 0 writes zeros.
+ *
+ *   x_bf16    [T][d] bf16 device, read
+ *   logits    [T][E] fp32 device, read (the router logits lcmoe_route
+ *             exports through logits_out)
+ *   counts    [E] int32 device, read (tokens per expert of the same routing)
+ *   n_groups  D >= 1, divides N
+ *   k_e       target FFN experts per token, 0 < k_e <= K
+ *   alpha, lambda  finite coefficients
+ *   stats     [2 + 2(D+1)] fp64 device, written: L_LB, L_Z, f_1..f_{D+1},
+ *             P_1..P_{D+1}
+ *   ws        >= lcmoe_router_stats_workspace_bytes(shape, n_groups) bytes
+ * Errors: INVALID_ARG (null pointer, T < 0, bad n_groups, k_e or
+ * coefficients), UNSUPPORTED (bad shape, misaligned x or logits), WORKSPACE,
+ * ERR_HIP. */
+size_t lcmoe_router_stats_workspace_bytes(const lcmoe_shape* shape, int32_t n_groups);
+lcmoe_status lcmoe_router_stats(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                const float* logits, const int32_t* counts, int32_t n_groups,
+                                double k_e, double alpha, double lambda, double* stats,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* lcmoe_status_str(lcmoe_status status);
 

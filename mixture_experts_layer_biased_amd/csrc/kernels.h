@@ -53,4 +53,10 @@ void launch_combine(const uint16_t* x, const uint16_t* Y, const int* idx, const 
 void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, double k_e,
                         float* bias, hipStream_t s);
 
+// Router-side statistics: kStatsBlocks partial rows of D+2 doubles in `part`.
+constexpr int kStatsBlocks = 1024;
+void launch_router_stats(const float* logits, const uint16_t* x, int T, int E, int d, int N, int D,
+                         int K, const int* counts, double k_e, double alpha, double lambda,
+                         double* part, double* stats, hipStream_t s);
+
 }  // namespace lcmoe

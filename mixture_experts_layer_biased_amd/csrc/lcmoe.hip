@@ -335,6 +335,33 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all, const in
   return hip_status();
 }
 
+size_t lcmoe_router_stats_workspace_bytes(const lcmoe_shape* shape, int32_t n_groups) {
+  if (check_shape(shape) != LCMOE_OK || n_groups < 1 || shape->n_ffn % n_groups != 0) return 0;
+  return (size_t)kStatsBlocks * (size_t)(n_groups + 2) * sizeof(double) + kAlign;
+}
+
+lcmoe_status lcmoe_router_stats(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                const float* logits, const int32_t* counts, int32_t n_groups,
+                                double k_e, double alpha, double lambda, double* stats,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (T < 0 || stats == nullptr || counts == nullptr || n_groups < 1 ||
+      shape->n_ffn % n_groups != 0 || !std::isfinite(k_e) || !(k_e > 0.0) ||
+      k_e > (double)shape->top_k || !std::isfinite(alpha) || !std::isfinite(lambda))
+    return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (x_bf16 == nullptr || logits == nullptr)) return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(x_bf16) || !aligned16(logits))) return LCMOE_ERR_UNSUPPORTED;
+  const size_t need = (size_t)kStatsBlocks * (size_t)(n_groups + 2) * sizeof(double);
+  char* base = ws_base(ws, ws_bytes, need);
+  if (base == nullptr) return LCMOE_ERR_WORKSPACE;
+  clear_hip_error();
+  launch_router_stats(logits, static_cast<const uint16_t*>(x_bf16), T, (int)n_experts(*shape),
+                      shape->d_model, shape->n_ffn, n_groups, shape->top_k, counts, k_e, alpha,
+                      lambda, reinterpret_cast<double*>(base), stats, stream);
+  return hip_status();
+}
+
 const char* lcmoe_status_str(lcmoe_status status) {
   switch (status) {
     case LCMOE_OK: return "LCMOE_OK";

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the layer runs in the HIP library.
 Names follow the C ABI (include/lcmoe.h): route, permute, forward,
-bias_update, workspace_bytes. Work is enqueued on torch's current stream.
+bias_update, router_stats, workspace_bytes. Work is enqueued on torch's current stream.
 If the library is missing, loading fails loudly; there is no fallback.
 """
 import ctypes
@@ -17,7 +17,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 W_BF16, W_FP8_E4M3_B128 = 0, 1
 
 EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
-           "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_status_str")
+           "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
+           "lcmoe_router_stats", "lcmoe_status_str")
 NUM_STAGES = 8
 STAGES = ("router", "topk", "permute", "gateup_small", "gateup_large", "down_small",
           "down_large", "combine")
@@ -78,6 +79,11 @@ def lib():
     L.lcmoe_forward_staged.restype = st
     L.lcmoe_bias_update.argtypes = [S, i32, _P, ctypes.c_double, ctypes.c_double, _P, _P]
     L.lcmoe_bias_update.restype = st
+    L.lcmoe_router_stats_workspace_bytes.argtypes = [S, i32]
+    L.lcmoe_router_stats_workspace_bytes.restype = sz
+    L.lcmoe_router_stats.argtypes = [S, i32, _P, _P, _P, i32, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_double, _P, _P, sz, _P]
+    L.lcmoe_router_stats.restype = st
     L.lcmoe_status_str.argtypes = [st]
     L.lcmoe_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -195,3 +201,28 @@ def bias_update(shape, counts, mu, k_e, bias, t_all):
                                    float(mu), float(k_e), _ptr(bias), _stream()),
            "lcmoe_bias_update")
     return bias
+
+
+def router_stats_workspace_bytes(shape, n_groups):
+    return int(lib().lcmoe_router_stats_workspace_bytes(ctypes.byref(shape), int(n_groups)))
+
+
+def router_stats(shape, x, logits, counts, n_groups, k_e, alpha=1.0, lam=1.0, ws=None):
+    """Device-level load-balance statistic (zero experts as group D+1) and the
+    hidden z-loss of x. `logits` [T,E] fp32 and `counts` [E] int32 come from
+    the same routing (route(..., logits=True)). Returns a device fp64 tensor
+    [2 + 2(D+1)]: L_LB, L_Z, f_1..f_{D+1}, P_1..P_{D+1}."""
+    T = x.shape[0]
+    dev = x.device
+    stats = torch.empty(2 + 2 * (int(n_groups) + 1), dtype=torch.float64, device=dev)
+    if ws is None:
+        n = router_stats_workspace_bytes(shape, n_groups)
+        if n == 0:
+            raise LcmoeError(ERR_INVALID_ARG, "invalid shape or n_groups")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    _dev(x, logits, counts, stats, ws)
+    _check(lib().lcmoe_router_stats(ctypes.byref(shape), T, _ptr(x), _ptr(logits), _ptr(counts),
+                                    int(n_groups), float(k_e), float(alpha), float(lam),
+                                    _ptr(stats), _ptr(ws), ws.numel(), _stream()),
+           "lcmoe_router_stats")
+    return stats

@@ -135,3 +135,33 @@ def test_workspace_monotone(dims):
     # large-shape workspace is dominated by the H and Y spills: T*min(K,N)*(I+d)*2
     d, N, Z, K, I = dims
     assert lcmoe.workspace_bytes(s, 8192) >= 8192 * min(K, N) * (I + d) * 2
+
+
+def _stats(shape, T, x=FAKE, lg=FAKE, c=FAKE, D=2, k_e=2.0, alpha=1.0, lam=1.0, st=FAKE, ws=None,
+           wsb=0):
+    L = lcmoe.lib()
+    return L.lcmoe_router_stats(ctypes.byref(shape), T, x, lg, c, D, k_e, alpha, lam, st, ws, wsb,
+                                None)
+
+
+def test_router_stats_validation():
+    s = shp()                      # N=8, Z=4, K=3
+    assert lcmoe.router_stats_workspace_bytes(s, 2) >= 256 * 4 * 8
+    for bad_d in (0, -1, 3, 16):
+        assert lcmoe.router_stats_workspace_bytes(s, bad_d) == 0
+        assert _stats(s, 4, D=bad_d) == ERR_INVALID_ARG
+    assert _stats(s, 4, k_e=0.0) == ERR_INVALID_ARG
+    assert _stats(s, 4, k_e=3.5) == ERR_INVALID_ARG      # k_e > K
+    assert _stats(s, 4, k_e=float("nan")) == ERR_INVALID_ARG
+    assert _stats(s, 4, alpha=float("inf")) == ERR_INVALID_ARG
+    assert _stats(s, 4, lam=float("nan")) == ERR_INVALID_ARG
+    assert _stats(s, -1) == ERR_INVALID_ARG
+    assert _stats(s, 4, st=None) == ERR_INVALID_ARG
+    assert _stats(s, 4, c=None) == ERR_INVALID_ARG
+    assert _stats(s, 4, x=None) == ERR_INVALID_ARG
+    assert _stats(s, 4, lg=None) == ERR_INVALID_ARG
+    assert _stats(s, 4, x=MIS) == ERR_UNSUPPORTED
+    assert _stats(s, 4, lg=MIS) == ERR_UNSUPPORTED
+    assert _stats(s, 4) == ERR_WORKSPACE
+    assert _stats(s, 4, ws=FAKE, wsb=64) == ERR_WORKSPACE
+    assert _stats(shp(n_ffn=0), 4) == ERR_INVALID_ARG
