@@ -17,6 +17,11 @@ from .lcmoe_oracle import (  # noqa: F401
     bf16_bits_to_f64,
     e4m3fn_value_table,
     dequant_fp8_blocks,
+    e4m3fn_encode,
+    quantize_rows_fp8,
+    dequant_rows_fp8,
+    round_to_bf16,
+    expert_ffn_a8,
     router_logits,
     selection_scores,
     select_topk,

@@ -30,6 +30,11 @@ Every function follows a passage of the "LongCat-Flash" llm-wiki entity page
            K_e : (K-K_e), even over the FFN groups, has f_j = 1 everywhere.
   R-zl     the hidden z-loss is taken over the layer input hidden states,
            i running over d_model.
+  R-a8     fp8 activations (with fp8 weights): each FFN expert's input row
+           (the token's x) and its intermediate row (H, after rounding to
+           bf16) are quantized per row: s = fl32(amax / 448) (1 for an
+           all-zero row), q = RNE to E4M3FN of fl32(v / s) clamped to +-448,
+           value q * s. Zero-computation experts see the exact x.
 
 Precision: all arithmetic on activations is fp64 except where a step is
 defined in fp32 (the selection score, the fp8 dequantised weight, the bias
@@ -88,6 +93,64 @@ def dequant_fp8_blocks(codes, scales, block=128):
     assert s.shape == (R // block, C // block)
     s_full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)
     return (q * s_full).astype(np.float32)
+
+
+def e4m3fn_encode(v):
+    """fp32 values -> OCP E4M3FN codes, round to nearest, ties to even.
+
+    Written from the format: normals are (1 + m/8) * 2^(e-7), e in 1..15
+    (e = 15 allows m <= 6; the largest finite value is 448), subnormals are
+    m/8 * 2^-6. |v| is split into its binary exponent, the fraction scaled to
+    eighths and rounded half-to-even (np.rint); a carry out of the mantissa
+    moves to the next exponent. Inputs must already lie in [-448, 448].
+    """
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    if np.any(np.abs(v) > 448.0) or np.any(np.isnan(v)):
+        raise ValueError("e4m3fn_encode needs finite inputs within +-448")
+    sign = np.signbit(v).astype(np.uint8) << 7
+    a = np.abs(v)
+    codes = np.zeros(a.shape, dtype=np.uint8)
+    sub = a < 2.0 ** -6
+    # subnormal range: multiples of 2^-9
+    m_sub = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)       # 0..8 (8 = min normal)
+    codes[sub] = np.where(m_sub == 8, 1 << 3, m_sub).astype(np.uint8)
+    an = a[~sub]
+    e = np.floor(np.log2(an)).astype(np.int64)
+    # guard the floating log2 at exact powers of two
+    e = np.where(2.0 ** (e + 1) <= an, e + 1, e)
+    e = np.where(2.0 ** e > an, e - 1, e)
+    m = np.rint((an / 2.0 ** e - 1.0) * 8.0).astype(np.int64)   # 0..8
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    codes[~sub] = (((e + 7) << 3) | m).astype(np.uint8)
+    return codes | sign
+
+
+def quantize_rows_fp8(v):
+    """Per-row activation quantization (reading R-a8): fp32 rows -> (codes
+    uint8, scale fp32 per row). s = fl32(amax / 448), 1 for an all-zero row;
+    q = e4m3fn_encode(clamp(fl32(v / s), -448, 448))."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.abs(v).max(axis=1)
+    s = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0))
+    s = s.astype(np.float32)
+    q = np.clip((v / s[:, None]).astype(np.float32), -448.0, 448.0)
+    return e4m3fn_encode(q), s
+
+
+def dequant_rows_fp8(codes, scales):
+    """q * s per row, in fp64 (every E4M3 value times an fp32 scale is exact
+    in fp64)."""
+    q = e4m3fn_value_table()[np.asarray(codes, dtype=np.uint8)]
+    return q * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+def round_to_bf16(v):
+    """fp64 -> fp32 -> bf16 (round to nearest even at each step), as fp64."""
+    u = np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------
@@ -205,12 +268,29 @@ def expert_ffn(x_rows, w13, w2):
     return h @ w2.T
 
 
-def combine_given_routing(x, idx, g, n_ffn, get_expert, tokens=None):
+def expert_ffn_a8(x_hat_rows, w13, w2):
+    """SiLU-gated FFN expert with fp8 activations (readings R-ffn, R-a8):
+    x_hat_rows are already quantized-dequantized; the intermediate
+    h = silu(x W1^T) * (x W3^T) is rounded to bf16, quantized per row, and
+    its dequantized value multiplies W2^T. fp64 otherwise."""
+    x_hat_rows = np.asarray(x_hat_rows, dtype=np.float64)
+    w13 = np.asarray(w13, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    inter = w2.shape[1]
+    u = x_hat_rows @ w13.T
+    h = round_to_bf16(silu(u[:, :inter]) * u[:, inter:])
+    hq, hs = quantize_rows_fp8(h.astype(np.float32))
+    return dequant_rows_fp8(hq, hs) @ w2.T
+
+
+def combine_given_routing(x, idx, g, n_ffn, get_expert, tokens=None, a8=False):
     """y_t = sum_k g[t,k] * (E_{idx[t,k]}(x_t) if idx[t,k] < N else x_t).
 
     x: [T, d] fp64 values; idx/g: [T, K]; get_expert(e) -> (w13_e, w2_e).
     tokens: optional subset of token indices to evaluate (others not computed);
     returns y rows for `tokens` (all tokens when None), fp64.
+    a8: FFN experts see each token row quantized per row to fp8 and quantize
+    their intermediate likewise (reading R-a8); zero experts see exact x.
     """
     x = np.asarray(x, dtype=np.float64)
     idx = np.asarray(idx)
@@ -225,10 +305,17 @@ def combine_given_routing(x, idx, g, n_ffn, get_expert, tokens=None):
     zero_mask = sub_idx >= n_ffn
     y += (sub_g * zero_mask).sum(axis=1)[:, None] * x[tokens]
     # FFN experts: evaluate each touched expert once on the tokens that chose it.
+    x_ffn = x[tokens]
+    if a8:
+        xq, xs = quantize_rows_fp8(x_ffn.astype(np.float32))
+        x_ffn = dequant_rows_fp8(xq, xs)
     for e in np.unique(sub_idx[~zero_mask]):
         rows, ks = np.nonzero(sub_idx == e)
         w13_e, w2_e = get_expert(int(e))
-        out = expert_ffn(x[tokens[rows]], w13_e, w2_e)
+        if a8:
+            out = expert_ffn_a8(x_ffn[rows], w13_e, w2_e)
+        else:
+            out = expert_ffn(x_ffn[rows], w13_e, w2_e)
         y[rows] += sub_g[rows, ks][:, None] * out
     return y
 

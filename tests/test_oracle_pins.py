@@ -491,3 +491,95 @@ def test_hidden_z_loss_closed_forms():
     assert math.isclose(oracle.hidden_z_loss(h, 0.3), want, rel_tol=1e-13)
     assert math.isclose(oracle.hidden_z_loss(-h, 0.3), want, rel_tol=1e-13)
     assert oracle.hidden_z_loss(np.zeros((0, 4)), 1.0) == 0.0
+
+
+# ----------------------------------------------------------------------------
+# fp8 activations (reading R-a8): the E4M3FN encoder, per-row quantization,
+# and the expert with quantized input and intermediate rows.
+# ----------------------------------------------------------------------------
+
+
+def test_e4m3fn_encoder_matches_torch():
+    vals = oracle.e4m3fn_value_table()
+    fin = np.sort(np.unique(np.abs(vals[np.isfinite(vals)])))
+    mids = (fin[1:] + fin[:-1]) / 2.0                 # exact ties: half-to-even
+    rng = np.random.default_rng(0)
+    rnd = np.exp(rng.uniform(-16, np.log(448.0), 20000)) * rng.choice([-1, 1], 20000)
+    edge = np.array([0.0, -0.0, 2.0 ** -6, 2.0 ** -9, 2.0 ** -10, 0.6 * 2.0 ** -9, 448.0, 440.0,
+                     2.0 ** -6 * (1 - 2.0 ** -4)])
+    v = np.concatenate([fin, -fin, mids, -mids, rnd, edge]).astype(np.float32)
+    got = oracle.e4m3fn_encode(v)
+    want = torch.tensor(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    # every code decodes back to its value
+    assert np.array_equal(oracle.e4m3fn_encode(fin.astype(np.float32)),
+                          np.array([np.flatnonzero(vals == f)[0] for f in fin], dtype=np.uint8))
+
+
+def test_quantize_rows_fp8_round_trip():
+    rng = np.random.default_rng(1)
+    v = (rng.normal(size=(40, 300)) * np.exp(rng.uniform(-6, 6, (40, 1)))).astype(np.float32)
+    v[3] = 0.0
+    codes, s = oracle.quantize_rows_fp8(v)
+    assert s[3] == 1.0 and not codes[3].any()
+    back = oracle.dequant_rows_fp8(codes, s)
+    amax = np.abs(v).max(axis=1)
+    assert np.allclose(s[amax > 0], (amax[amax > 0] / np.float32(448)).astype(np.float32), rtol=0)
+    normal = np.abs(v) >= 2.0 ** -6 * s[:, None]
+    err = np.abs(back - v)
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(v[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0 ** -10 * np.broadcast_to(s[:, None], v.shape)[~normal] * (1 + 1e-6))
+    # the row maximum lands on +-448 (or one step below it after rounding)
+    top = np.abs(oracle.e4m3fn_value_table()[codes[amax > 0, np.abs(v[amax > 0]).argmax(1)]])
+    assert np.all(top >= 416.0)
+
+
+def test_round_to_bf16_matches_torch():
+    rng = np.random.default_rng(2)
+    v = rng.normal(size=5000) * np.exp(rng.uniform(-20, 20, 5000))
+    got = oracle.round_to_bf16(v)
+    want = torch.tensor(v).float().to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, want)
+
+
+def test_a8_expert_matches_torch_composition():
+    # The same expert built from torch primitives: per-row scales, torch's
+    # float8_e4m3fn cast, float64 matmuls, torch's bf16 rounding of H.
+    rng = np.random.default_rng(3)
+    d, inter, m = 256, 128, 9
+    x = rng.normal(size=(m, d)).astype(np.float32)
+    w13 = (rng.normal(size=(2 * inter, d)) * 0.05).astype(np.float32)
+    w2 = (rng.normal(size=(d, inter)) * 0.05).astype(np.float32)
+
+    def tq(a):  # torch per-row quantize-dequantize
+        a = torch.tensor(a, dtype=torch.float32)
+        amax = a.abs().amax(dim=1)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (a / s[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).double()
+        return (q * s.double()[:, None])
+
+    xh = tq(x)
+    u = xh @ torch.tensor(w13, dtype=torch.float64).T
+    h = (torch.nn.functional.silu(u[:, :inter]) * u[:, inter:]).float().to(torch.bfloat16)
+    want = (tq(h.float().numpy()) @ torch.tensor(w2, dtype=torch.float64).T).numpy()
+    xq, xs = oracle.quantize_rows_fp8(x)
+    got = oracle.expert_ffn_a8(oracle.dequant_rows_fp8(xq, xs), w13, w2)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # and it is a perturbation of the unquantized expert of the expected size
+    ref = oracle.expert_ffn(x, w13, w2)
+    rel = np.abs(got - ref).max() / np.abs(ref).max()
+    assert 1e-4 < rel < 0.1
+
+
+def test_a8_zero_routing_is_exact_identity():
+    # FFN experts biased out: y = (sum_k g) x exactly, the identity sees exact x.
+    cfg = inputs.CONFIGS["tiny"]
+    L = inputs.make_layer(cfg, "cpu")
+    x = bf16_values(inputs.make_tokens(cfg, "cpu"))
+    b = L["bias"].numpy().copy()
+    b[: cfg.n_ffn] = -1e4
+    r = oracle.route(x, L["w_router"].numpy(), b, cfg.k)
+    assert np.all(r["idx"] >= cfg.n_ffn)
+    get = expert_getter(L, cfg)
+    y = oracle.combine_given_routing(x, r["idx"], r["g"], cfg.n_ffn, get, a8=True)
+    assert np.array_equal(y, r["g"].sum(1)[:, None] * x)
