@@ -6,7 +6,8 @@ SiLU-gated expert GEMMs, combine) on a resident batch of synthetic tokens at
 the model's layer shape (d_model 6144, 512 FFN + 256 zero-computation
 experts, K=12, expert intermediate 2048; "LongCat-Flash" llm-wiki entity
 page, section 1 table). The headline value is the prefill batch (T=8192,
-bf16); the decode batch (T=64, bf16) and the fp8-weight batch (T=16384) are
+bf16); the decode batch (T=64, bf16), the fp8-weight batch (T=16384), the
+same batch with fp8 activations as well, and a 32768-token bf16 batch are
 measured in the same run and reported alongside.
 
 Per-stage kernel durations come from HIP events recorded between the
@@ -30,6 +31,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 4 << 30      # the calibration copy of copy_bandwidth()
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 MFMA (fp8 weights run bf16 MFMA)
+PEAK_FP8 = 5.0e15          # FLOP/s, dense fp8 MFMA (fp8 weights and fp8 activations)
+
+
+def mfma_peak(cfg):
+    """Peak of the contraction's own dtype."""
+    return PEAK_FP8 if cfg.wdtype == "fp8a8" else PEAK_BF16
 
 
 def _hip():
@@ -192,8 +199,8 @@ def kernel_work(cfg, counts):
     """
     N, d, I = cfg.n_ffn, cfg.d, cfg.inter
     c = counts[:N].astype(np.int64)
-    sw = 1 if cfg.wdtype == "fp8" else 2
-    sc = (4 / (128 * 128)) if cfg.wdtype == "fp8" else 0.0
+    sw = 1 if cfg.wdtype in ("fp8", "fp8a8") else 2
+    sc = (4 / (128 * 128)) if cfg.wdtype in ("fp8", "fp8a8") else 0.0
     out = {}
     for path, sel in (("small", (c >= 1) & (c <= 32)), ("large", c > 32)):
         et, rows = int(sel.sum()), int(c[sel].sum())
@@ -210,7 +217,7 @@ def layer_bytes(cfg, counts, T):
     """Whole-layer algorithmic bytes: touched experts' weights once, the router
     weights once, x read once and y written once."""
     N, d, I, E = cfg.n_ffn, cfg.d, cfg.inter, cfg.n_experts
-    sw = 1 if cfg.wdtype == "fp8" else 2
+    sw = 1 if cfg.wdtype in ("fp8", "fp8a8") else 2
     et = int((counts[:N] > 0).sum())
     return et * 3 * I * d * sw + E * d * 4 + 2 * T * d * 2
 
@@ -260,11 +267,12 @@ def measure(cfg, steps, warmup, hip):
     dom = max(gemm, key=lambda k: stages[k])
     wk = work[dom]
     dom_s = stages[dom] / 1e3
-    bound = "hbm" if wk["flops"] / wk["bytes"] < PEAK_BF16 / PEAK_HBM else "mfma"
+    peak_mfma = mfma_peak(cfg)
+    bound = "hbm" if wk["flops"] / wk["bytes"] < peak_mfma / PEAK_HBM else "mfma"
     if bound == "hbm":
         ach, peak, unit = wk["bytes"] / dom_s / 1e9, PEAK_HBM / 1e9, "GB/s"
     else:
-        ach, peak, unit = wk["flops"] / dom_s / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
+        ach, peak, unit = wk["flops"] / dom_s / 1e12, peak_mfma / 1e12, "TFLOP/s"
     gemm_s = sum(stages[k] for k in work) / 1e3
     gemm_flops = sum(w["flops"] for w in work.values())
     gemm_bytes = sum(w["bytes"] for w in work.values())
@@ -279,10 +287,10 @@ def measure(cfg, steps, warmup, hip):
         roofline=dict(bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                       traffic=measured_traffic(cfg.name, dom), algorithmic_bytes=wk["bytes"],
                       flops=wk["flops"], kernel_ms=stages[dom]),
-        grouped_gemm=dict(ms=gemm_s * 1e3, mfma_frac=gemm_flops / gemm_s / PEAK_BF16,
+        grouped_gemm=dict(ms=gemm_s * 1e3, mfma_frac=gemm_flops / gemm_s / peak_mfma,
                           hbm_frac=gemm_bytes / gemm_s / PEAK_HBM),
         layer=dict(algorithmic_bytes=lb, hbm_frac=lb / (ms / 1e3) / PEAK_HBM,
-                   mfma_frac=gemm_flops / (ms / 1e3) / PEAK_BF16),
+                   mfma_frac=gemm_flops / (ms / 1e3) / peak_mfma),
     )
     # Router-side statistics (outside the layer step): one routing call that
     # exports the logits, then lcmoe_router_stats timed on its own.
@@ -371,7 +379,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "fp8", "prefill32k"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "fp8", "fp8a8", "prefill32k"], default=None,
                     help="measure a single configuration (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=160)
@@ -402,7 +410,7 @@ def main():
     print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read+write)", file=sys.stderr, flush=True)
     results = {}
     baseline = None
-    names = [args.only] if args.only else ["prefill", "decode", "fp8", "prefill32k"]
+    names = [args.only] if args.only else ["prefill", "decode", "fp8", "fp8a8", "prefill32k"]
     for name in names:
         cfg = inputs.CONFIGS[name]
         res, keep = measure(cfg, args.steps, args.warmup, hip)
@@ -430,7 +438,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.wdtype == "bf16" else "fp8-e4m3 weights, bf16 MFMA",
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 MFMA",
+                  "fp8a8": "fp8-e4m3 weights and activations, fp8 MFMA"}[cfg.wdtype],
         "data": "synthetic",
         "config": {"workload": (f"LongCat-shape MoE layer, {main_name} batch: T={cfg.tokens}, "
                                 f"d_model={cfg.d}, {cfg.n_ffn} FFN + {cfg.n_zero} zero experts, "

@@ -69,7 +69,16 @@ typedef enum {
 
 typedef enum {
   LCMOE_W_BF16 = 0,          /* expert weights in bf16                         */
-  LCMOE_W_FP8_E4M3_B128 = 1  /* E4M3FN codes + fp32 scale per 128x128 block    */
+  LCMOE_W_FP8_E4M3_B128 = 1, /* E4M3FN codes + fp32 scale per 128x128 block    */
+  /* Weights as LCMOE_W_FP8_E4M3_B128, and fp8 activations: each FFN expert's
+   * input row (x_t) and intermediate row (H, after its bf16 rounding) are
+   * quantized per row to E4M3FN with one fp32 scale s = fl32(amax/448)
+   * (1 for a zero row), q = round-to-nearest-even of fl32(v/s), and the
+   * expert GEMMs run on fp8 MFMA (fp32 accumulation, weight block scales
+   * applied per 128-wide k block, the row scale after the sum). The pages
+   * name FP8 quantization without its activation scheme; this is the
+   * reading. Zero-computation experts still return the exact x. */
+  LCMOE_W_FP8_E4M3_B128_A8 = 2
 } lcmoe_wdtype;
 
 /* Layer shape. Model table of "LongCat-Flash" (section 1): d_model 6144,

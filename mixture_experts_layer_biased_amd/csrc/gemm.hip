@@ -546,6 +546,236 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
 }
 
 // ===========================================================================
+// large-M kernel with fp8 weights and fp8 activations
+//
+// Same tiles, tile order and direct-to-LDS ring as above, with both operands
+// E4M3FN codes: a stage is 128 k = one whole 128-byte line of every x (or H)
+// row and every weight row (eight lanes per row, eight rows per copy), and
+// one 128-wide weight-scale block. Per stage and 32x32 fragment pair, two
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0 scales) accumulate the raw
+// code products of the block into a fresh fp32 tile T, then acc += T * s_w
+// (the weight block scale, a wave-uniform value). The per-row activation
+// scale multiplies the finished accumulator in the epilogue.
+//
+// MFMA operand (both sides identically): lane l supplies row (l & 31) and
+// bytes 32 (l >> 5) + [0, 32) of the 64-wide k step, i.e. chunks
+// 4 m + 2 h and 4 m + 2 h + 1 of the stage's 128-byte row for step m; the
+// 128-byte-row swizzle c ^ ((r >> 1) & 7) keeps each 16-lane read
+// conflict-free.
+// ===========================================================================
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
+  i32x8_t r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void gemm_big_a8_kernel(GemmArgs a) {
+  constexpr int LDS_CHUNKS = 9216;       // 144 KB
+  constexpr int MAX_SLOTS = 3;
+  constexpr int B_CHUNKS = 256 * 8;      // 256 weight rows x 128 B
+  constexpr int ROWS = kBigTileRows;     // 320 token rows
+  constexpr int AG = ROWS / 8 / 8;       // x copy groups per wave (5)
+  constexpr int BG = 4;                  // weight copy groups per wave
+  constexpr int MF = ROWS / 64;          // token fragments per wave (5)
+  constexpr int SK = 128;                // k per stage
+  __shared__ uint4 lds[LDS_CHUNKS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int h = lane >> 5, lrow = lane & 31;
+  const int kdim = a.kdim;  // elements = bytes per row
+
+  const int total = a.meta[1] * a.nslices;
+  const int per_xcd = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  if (pos >= per_xcd) return;
+  const int L = xcd * per_xcd + pos;
+  if (L >= total) return;
+  int lo = 0, hi = a.n_ffn - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.mt_prefix[mid] * a.nslices <= L) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int mt = a.mt_prefix[e + 1] - a.mt_prefix[e];
+  const int local = L - a.mt_prefix[e] * a.nslices;
+  const int slice = local / mt, m = local - slice * mt;
+  const int cnt = a.counts[e];
+  const int r0 = (int)((long long)m * cnt / mt);
+  const int rows = (int)((long long)(m + 1) * cnt / mt) - r0;
+  const int rowbase = a.offsets[e] + r0;
+
+  auto wrow_of = [&](int j) -> int {
+    if (GATEUP) {
+      const int col = slice * kBigColsGateUp + (j & 127);
+      if (col >= a.n_out) return -1;
+      return j < 128 ? col : a.n_out + col;
+    } else {
+      const int col = slice * kBigColsDown + j;
+      return col < a.n_out ? col : -1;
+    }
+  };
+
+  // Copies: 8-row groups w + 8 g2 of the x (or H) codes and of the weight
+  // codes, eight lanes per 128-byte row; byte offsets from the operand bases.
+  uint32_t aoff[AG], boff[BG];
+  bool ause[AG], buse[BG];
+  const char* wexp = static_cast<const char*>(a.w) + (size_t)e * a.rows_total * kdim;
+  const char* abase = reinterpret_cast<const char*>(a.src8) + (GATEUP ? 0 : (size_t)rowbase * kdim);
+  const int ac = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+#pragma unroll
+  for (int g2 = 0; g2 < AG; ++g2) {
+    const int g = wave + 8 * g2;
+    const int row = 8 * g + (lane >> 3);
+    ause[g2] = 8 * g < rows;
+    const int rr = row < rows ? row : 0;
+    const size_t srow = GATEUP ? (size_t)(a.perm[rowbase + rr] / a.topk) : (size_t)rr;
+    aoff[g2] = (uint32_t)(srow * kdim + 16 * ac);
+  }
+#pragma unroll
+  for (int g2 = 0; g2 < BG; ++g2) {
+    const int g = wave + 8 * g2;
+    const int row = 8 * g + (lane >> 3);
+    const int wr = wrow_of(row);
+    buse[g2] = wrow_of(8 * g) >= 0;
+    boff[g2] = (uint32_t)((size_t)(wr >= 0 ? wr : 0) * kdim + 16 * ac);
+  }
+  int per_stage = 0;
+#pragma unroll
+  for (int g2 = 0; g2 < AG; ++g2) per_stage += (int)ause[g2];
+#pragma unroll
+  for (int g2 = 0; g2 < BG; ++g2) per_stage += (int)buse[g2];
+  const int nst = kdim / SK;
+  const int a_chunks = ((rows + 7) >> 3) * 64;
+  const int slot = a_chunks + B_CHUNKS;
+  const int nslots = min(MAX_SLOTS, LDS_CHUNKS / slot);
+
+  auto issue = [&](int s) {
+    const char* xs = abase + (size_t)s * SK;
+    const char* ws = wexp + (size_t)s * SK;
+    const uint4* base = lds + (s % nslots) * slot;
+#pragma unroll
+    for (int g2 = 0; g2 < BG; ++g2)
+      if (buse[g2]) dma16(ws, boff[g2], base + a_chunks + (wave + 8 * g2) * 64);
+#pragma unroll
+    for (int g2 = 0; g2 < AG; ++g2)
+      if (ause[g2]) dma16(xs, aoff[g2], base + (wave + 8 * g2) * 64);
+  };
+
+  f32x16_t acc[MF][2];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
+  auto frow = [&](int j) { return 32 * (2 * j + wm); };
+  const int bbase0 = GATEUP ? 32 * wn : 64 * wn;
+  const int bbase1 = GATEUP ? 128 + 32 * wn : 64 * wn + 32;
+
+  // Weight block scales for every 128-wide k block (one per stage) of the
+  // tile's two 128-row weight blocks (gate/up: the gate and the up block of
+  // the slice; down: blocks 2 slice and 2 slice + 1), staged in LDS once.
+  // Wave-uniform reads per stage: fragment f uses row sq[f].
+  __shared__ float sscale[2][128];
+  const int kblocks = kdim >> 7;
+  for (int j = tid; j < 2 * kblocks; j += 512) {
+    const int q = j / kblocks, kb = j - q * kblocks;
+    const int brow = GATEUP ? (q ? (a.n_out >> 7) + slice : slice) : 2 * slice + q;
+    sscale[q][kb] = brow < (a.rows_total >> 7)
+                        ? a.wscale[((size_t)e * (a.rows_total >> 7) + brow) * kblocks + kb]
+                        : 0.f;
+  }
+  const int sq0 = GATEUP ? 0 : (wn >> 1), sq1 = GATEUP ? 1 : (wn >> 1);
+  wait_vmcnt<0>();
+  __syncthreads();
+  const int nact = __builtin_amdgcn_readfirstlane(
+      max(0, min(MF, (rows - 32 * wm + 63) / 64)));
+  const int sw = (lrow >> 1) & 7;  // swizzle term of every row this lane reads
+
+  auto compute = [&](auto NA_c, int s) {
+    constexpr int NA = decltype(NA_c)::value;
+    const uint4* A = lds + (s % nslots) * slot + frow(0) * 8 + lrow * 8;
+    const uint4* B = lds + (s % nslots) * slot + a_chunks + lrow * 8;
+    const float s0 = sscale[sq0][s], s1 = sscale[sq1][s];
+    i32x8_t Bv[2][2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int c0 = (4 * mm + 2 * h) ^ sw, c1 = (4 * mm + 2 * h + 1) ^ sw;
+      Bv[mm][0] = as_i32x8(B[bbase0 * 8 + c0], B[bbase0 * 8 + c1]);
+      Bv[mm][1] = as_i32x8(B[bbase1 * 8 + c0], B[bbase1 * 8 + c1]);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      i32x8_t Av[2];
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int c0 = (4 * mm + 2 * h) ^ sw, c1 = (4 * mm + 2 * h + 1) ^ sw;
+        const int rb = (frow(i) - frow(0)) * 8;
+        Av[mm] = as_i32x8(A[rb + c0], A[rb + c1]);
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        f32x16_t t;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) t[v] = 0.f;
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av[0], Bv[0][f], t, 0, 0, 0, 127, 0, 127);
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av[1], Bv[1][f], t, 0, 0, 0, 127, 0, 127);
+        const float sc = f ? s1 : s0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][f][v] = __builtin_fmaf(t[v], sc, acc[i][f][v]);
+      }
+    }
+  };
+  auto kloop = [&](auto NA_c) {
+    for (int s = 0; s < nslots - 1 && s < nst; ++s) issue(s);
+    for (int s = 0; s < nst; ++s) {
+      wait_vmcnt_upto(per_stage * min(nslots - 2, nst - 1 - s));
+      raw_barrier();
+      if (s + nslots - 1 < nst) issue(s + nslots - 1);
+      compute(NA_c, s);
+    }
+  };
+  switch (nact) {
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
+  }
+
+  // Epilogue: the per-row activation scale, then SiLU-gating (gate/up) or
+  // the store of Y (down).
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    if (frow(i) >= rows) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tr = frow(i) + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (tr >= rows) continue;
+      const float sa = GATEUP ? a.ascale[a.perm[rowbase + tr] / a.topk] : a.ascale[rowbase + tr];
+      uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
+      if (GATEUP) {
+        const int col = slice * kBigColsGateUp + 32 * wn + lrow;
+        if (col < a.n_out)
+          orow[col] = f32_to_bf16(silu_f(acc[i][0][v] * sa) * (acc[i][1][v] * sa));
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int col = slice * kBigColsDown + 64 * wn + 32 * f + lrow;
+          if (col < a.n_out) orow[col] = f32_to_bf16(acc[i][f][v] * sa);
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // launchers
 // ===========================================================================
 void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s) {
@@ -566,6 +796,11 @@ void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStre
     if (fp8) gemm_big_dma_kernel<false, true><<<grid, 512, 0, s>>>(a);
     else gemm_big_dma_kernel<false, false><<<grid, 512, 0, s>>>(a);
   }
+}
+
+void launch_gemm_big_a8(const GemmArgs& a, bool gateup, int grid, hipStream_t s) {
+  if (gateup) gemm_big_a8_kernel<true><<<grid, 512, 0, s>>>(a);
+  else gemm_big_a8_kernel<false><<<grid, 512, 0, s>>>(a);
 }
 
 }  // namespace lcmoe

@@ -23,6 +23,8 @@ struct GemmArgs {
   const void* w;           // expert weights [N][rows_total][kdim], bf16 or fp8 codes
   const float* wscale;     // fp8: [N][rows_total/128][kdim/128]
   const uint16_t* src;     // gate/up: x [T][d]; down: H [S][I]
+  const uint8_t* src8;     // fp8 activations: E4M3FN codes of src, same layout
+  const float* ascale;     // fp8 activations: per-row scale (gate/up: [T]; down: [S])
   const int* perm;         // FFN slot ids grouped by expert (gate/up gather)
   const int* offsets;      // [N+1]
   const int* counts;       // [E]
@@ -48,6 +50,14 @@ void launch_permute(const int* idx, int T, int K, int E, int N, int ntile,
                     int* row_of_slot, hipStream_t s);
 void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
 void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
+// Large-M GEMM with fp8 weights and fp8 activations (src8, ascale).
+void launch_gemm_big_a8(const GemmArgs& a, bool gateup, int grid, hipStream_t s);
+// Per-row E4M3FN quantization of bf16 rows: q [rows][cols] codes, scale
+// [rows] = amax/448 (1 for a zero row), deq [rows][cols] bf16(fl32(q) * s)
+// (may alias src). The row count is read on the device (*rows_dev) when
+// rows_dev is not null, else `rows`; grid-stride over rows.
+void launch_quant_rows(const uint16_t* src, int rows, const int* rows_dev, int cols, uint8_t* q,
+                       float* scale, uint16_t* deq, int grid, hipStream_t s);
 void launch_combine(const uint16_t* x, const uint16_t* Y, const int* idx, const float* gate,
                     const int* row_of_slot, int T, int d, int K, uint16_t* y, hipStream_t s);
 void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, double k_e,

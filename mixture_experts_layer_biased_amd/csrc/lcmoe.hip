@@ -19,7 +19,7 @@ struct Layout {
   long long smax = 0;
   size_t zpart = 0, masks = 0, tilecnt = 0, tileoff = 0, offsets = 0, small_list = 0,
          mt_prefix = 0, meta = 0, routing_end = 0, perm = 0, row_of_slot = 0, permute_end = 0,
-         H = 0, Y = 0, total = 0;
+         H = 0, Y = 0, xq = 0, xs = 0, xdeq = 0, hq = 0, hs = 0, total = 0;
 };
 
 inline long long n_experts(const lcmoe_shape& s) { return (long long)s.n_ffn + s.n_zero; }
@@ -29,14 +29,15 @@ lcmoe_status check_shape(const lcmoe_shape* s) {
   if (s->n_ffn < 1 || s->n_zero < 0 || s->top_k < 1 || s->d_model < 1 || s->d_expert < 1)
     return LCMOE_ERR_INVALID_ARG;
   if (s->top_k > n_experts(*s)) return LCMOE_ERR_INVALID_ARG;
-  if (s->w_dtype != LCMOE_W_BF16 && s->w_dtype != LCMOE_W_FP8_E4M3_B128)
+  if (s->w_dtype != LCMOE_W_BF16 && s->w_dtype != LCMOE_W_FP8_E4M3_B128 &&
+      s->w_dtype != LCMOE_W_FP8_E4M3_B128_A8)
     return LCMOE_ERR_INVALID_ARG;
   if (s->top_k > 64 || n_experts(*s) > 2048) return LCMOE_ERR_UNSUPPORTED;
   if (s->d_model % 32 != 0 || s->d_expert % 32 != 0) return LCMOE_ERR_UNSUPPORTED;
   // One expert's gate/up matrix is addressed with 32-bit byte offsets.
-  const long long wbytes = s->w_dtype == LCMOE_W_FP8_E4M3_B128 ? 1 : 2;
+  const long long wbytes = s->w_dtype == LCMOE_W_BF16 ? 2 : 1;
   if (2ll * s->d_expert * s->d_model * wbytes >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
-  if (s->w_dtype == LCMOE_W_FP8_E4M3_B128 &&
+  if (s->w_dtype != LCMOE_W_BF16 &&
       (s->d_model % 128 != 0 || s->d_expert % 128 != 0 || s->d_model > 16384 ||
        s->d_expert > 16384))
     return LCMOE_ERR_UNSUPPORTED;
@@ -81,6 +82,15 @@ Layout make_layout(const lcmoe_shape& s, int T) {
   L.smax = (long long)T * std::min(K, N);
   L.H = take((size_t)L.smax * s.d_expert * 2);
   L.Y = take((size_t)L.smax * s.d_model * 2);
+  if (s.w_dtype == LCMOE_W_FP8_E4M3_B128_A8) {
+    // fp8 activations: codes and per-row scales of x and of H, and the
+    // dequantized bf16 x the small-M path reads.
+    L.xq = take((size_t)T * s.d_model);
+    L.xs = take((size_t)T * 4);
+    L.xdeq = take((size_t)T * s.d_model * 2);
+    L.hq = take((size_t)L.smax * s.d_expert);
+    L.hs = take((size_t)L.smax * 4);
+  }
   L.total = off;
   return L;
 }
@@ -207,7 +217,8 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
                                   hipStream_t stream, hipEvent_t* stage_events) {
   lcmoe_status st = check_shape(shape);
   if (st != LCMOE_OK) return st;
-  const bool fp8 = shape->w_dtype == LCMOE_W_FP8_E4M3_B128;
+  const bool fp8 = shape->w_dtype != LCMOE_W_BF16;          // fp8 weights
+  const bool a8 = shape->w_dtype == LCMOE_W_FP8_E4M3_B128_A8;  // and fp8 activations
   if (T < 0 || counts == nullptr) return LCMOE_ERR_INVALID_ARG;
   if (T > 0 && (x_bf16 == nullptr || w_router == nullptr || bias == nullptr || w13 == nullptr ||
                 w2 == nullptr || y_bf16 == nullptr || topk_idx == nullptr ||
@@ -247,6 +258,10 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
                    at<unsigned long long>(base, L.masks), at<int>(base, L.tilecnt),
                    at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.small_list),
                    at<int>(base, L.mt_prefix), at<int>(base, L.meta), perm, row_of_slot, stream);
+    if (a8)  // fp8 activations: quantize x per row (timed with the permutation stage)
+      launch_quant_rows(static_cast<const uint16_t*>(x_bf16), T, nullptr, shape->d_model,
+                        at<uint8_t>(base, L.xq), at<float>(base, L.xs),
+                        at<uint16_t>(base, L.xdeq), std::min(2048, (T + 3) / 4), stream);
     mark(ev, 3, stream);
   }
 
@@ -281,7 +296,11 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
   // gate/up: H = silu(X W1^T) * (X W3^T)
   a.w = w13;
   a.wscale = w13_scale;
-  a.src = static_cast<const uint16_t*>(x_bf16);
+  // The small-M path reads bf16 activations: with fp8 activations, the
+  // dequantized rows fl32(q) * s rounded to bf16.
+  a.src = a8 ? at<uint16_t>(base, L.xdeq) : static_cast<const uint16_t*>(x_bf16);
+  a.src8 = a8 ? at<uint8_t>(base, L.xq) : nullptr;
+  a.ascale = a8 ? at<float>(base, L.xs) : nullptr;
   a.out = H;
   a.kdim = d;
   a.n_out = I;
@@ -290,13 +309,20 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
   launch_gemm_small(a, true, fp8, small_grid(a.nslices), stream);
   mark(ev, 4, stream);
   a.nslices = (I + kBigColsGateUp - 1) / kBigColsGateUp;
-  launch_gemm_big(a, true, fp8, big_grid(a.nslices), stream);
+  if (a8) launch_gemm_big_a8(a, true, big_grid(a.nslices), stream);
+  else launch_gemm_big(a, true, fp8, big_grid(a.nslices), stream);
   mark(ev, 5, stream);
+  if (a8)  // quantize the S rows of H (S read on the device), dequantized copy in place
+    launch_quant_rows(H, 0, at<int>(base, L.meta) + 2, I, at<uint8_t>(base, L.hq),
+                      at<float>(base, L.hs), H, (int)std::min<long long>(2048, (smax + 3) / 4),
+                      stream);
 
   // down: Y = H W2^T
   a.w = w2;
   a.wscale = w2_scale;
   a.src = H;
+  a.src8 = a8 ? at<uint8_t>(base, L.hq) : nullptr;
+  a.ascale = a8 ? at<float>(base, L.hs) : nullptr;
   a.out = Y;
   a.kdim = I;
   a.n_out = d;
@@ -305,7 +331,8 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
   launch_gemm_small(a, false, fp8, small_grid(a.nslices), stream);
   mark(ev, 6, stream);
   a.nslices = (d + kBigColsDown - 1) / kBigColsDown;
-  launch_gemm_big(a, false, fp8, big_grid(a.nslices), stream);
+  if (a8) launch_gemm_big_a8(a, false, big_grid(a.nslices), stream);
+  else launch_gemm_big(a, false, fp8, big_grid(a.nslices), stream);
   mark(ev, 7, stream);
 
   launch_combine(static_cast<const uint16_t*>(x_bf16), Y, topk_idx, topk_gate, row_of_slot, T,

@@ -31,7 +31,7 @@ class LayerConfig:
     inter: int        # expert intermediate size I
     tokens: int       # T
     seed: int
-    wdtype: str = "bf16"          # "bf16" or "fp8"
+    wdtype: str = "bf16"          # "bf16", "fp8" (weights) or "fp8a8" (weights and activations)
     bias_std: float = 0.0         # router bias ~ N(0, bias_std) over all E, 0 -> zeros
     skew_frac: float = 0.0        # fraction of tokens scaled by skew_factor
     skew_factor: float = 1.0
@@ -60,6 +60,10 @@ CONFIGS = {
     # followed by 20 bias-update steps (mu=1e-3, K_e=8) on fresh batches.
     "fp8": LayerConfig("fp8", 6144, 512, 256, 12, 2048, 16384, seed=5, wdtype="fp8",
                        extra=dict(bias_steps=20, mu=1e-3, k_e=8.0)),
+    # The fp8 configuration's layer and tokens with fp8 activations as well
+    # (per-row E4M3FN quantization of expert inputs and intermediates, fp8
+    # MFMA); same seed, so the same weights and tokens as "fp8".
+    "fp8a8": LayerConfig("fp8a8", 6144, 512, 256, 12, 2048, 16384, seed=5, wdtype="fp8a8"),
     # LongCat shape, bf16, T=32768 (about 512 rows per FFN expert): the batch
     # at which the bf16 grouped GEMM has more MFMA work than weight bytes
     # (512 FLOP/B). An extra measurement point, not one of the five above.
@@ -134,7 +138,7 @@ def make_layer(cfg, device):
     w_router, bias = make_router(cfg, device)
     g13 = _gen(device, cfg.seed, 2)
     g2 = _gen(device, cfg.seed, 3)
-    fp8 = cfg.wdtype == "fp8"
+    fp8 = cfg.wdtype in ("fp8", "fp8a8")
     wdt = torch.uint8 if fp8 else torch.bfloat16
     w13 = torch.empty(N, 2 * I, d, device=device, dtype=wdt)
     w2 = torch.empty(N, d, I, device=device, dtype=wdt)

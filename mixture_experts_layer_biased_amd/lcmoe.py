@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblcmoe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-W_BF16, W_FP8_E4M3_B128 = 0, 1
+W_BF16, W_FP8_E4M3_B128, W_FP8_E4M3_B128_A8 = 0, 1, 2
 
 EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
            "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
@@ -42,7 +42,7 @@ class Shape(ctypes.Structure):
 
 def make_shape(d_model, n_ffn, n_zero, top_k, d_expert, w_dtype=W_BF16):
     if isinstance(w_dtype, str):
-        w_dtype = {"bf16": W_BF16, "fp8": W_FP8_E4M3_B128}[w_dtype]
+        w_dtype = {"bf16": W_BF16, "fp8": W_FP8_E4M3_B128, "fp8a8": W_FP8_E4M3_B128_A8}[w_dtype]
     return Shape(d_model, n_ffn, n_zero, top_k, d_expert, w_dtype)
 
 

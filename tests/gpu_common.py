@@ -43,7 +43,7 @@ def oracle_forward_rows(cfg, L, x, idx_gpu, tokens, cache=None):
     idx = idx_gpu[tokens]
     g, _ = oracle.softmax_gates(z, idx)
     get = expert_getter(L, cfg.wdtype, cache=cache)
-    return oracle.combine_given_routing(xv, idx, g, cfg.n_ffn, get)
+    return oracle.combine_given_routing(xv, idx, g, cfg.n_ffn, get, a8=cfg.wdtype == "fp8a8")
 
 
 def router_error_scale(x_vals, w_router, d):

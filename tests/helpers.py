@@ -27,7 +27,7 @@ def expert_getter(layer, wdtype, cache=None):
     def get(e):
         if cache is not None and e in cache:
             return cache[e]
-        if wdtype == "fp8":
+        if wdtype in ("fp8", "fp8a8"):
             a = oracle.dequant_fp8_blocks(w13[e].cpu().numpy(), s13[e].cpu().numpy())
             b = oracle.dequant_fp8_blocks(w2[e].cpu().numpy(), s2[e].cpu().numpy())
             out = (a.astype(np.float64), b.astype(np.float64))

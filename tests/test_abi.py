@@ -41,6 +41,13 @@ def test_library_exports_every_declared_function():
     assert set(decl) <= syms
 
 
+def test_library_has_no_undefined_internal_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", lcmoe.LIB_PATH],
+                         capture_output=True, text=True).stdout
+    assert "lcmoe" not in out, out
+
+
 def test_status_strings():
     assert lcmoe.status_str(0) == "LCMOE_OK"
     assert lcmoe.status_str(3) == "LCMOE_ERR_WORKSPACE"
@@ -79,6 +86,8 @@ def shp(**kw):
     (dict(d_model=48), ERR_UNSUPPORTED),
     (dict(d_expert=40), ERR_UNSUPPORTED),
     (dict(w_dtype=1), ERR_UNSUPPORTED),            # fp8 needs d, I % 128 == 0
+    (dict(w_dtype=2), ERR_UNSUPPORTED),            # fp8 activations too
+    (dict(w_dtype=3), ERR_INVALID_ARG),
     (dict(d_model=32768, d_expert=32768), ERR_UNSUPPORTED),  # one W13 of 4 GiB
 ])
 def test_invalid_shapes(kw, status):

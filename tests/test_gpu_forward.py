@@ -16,7 +16,7 @@ from tests.helpers import bf16_values
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "fp8": 5e-2}
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "fp8a8": 5e-2}
 
 
 def run_forward(cfg, L, x):
@@ -58,6 +58,17 @@ def test_forward_all_tokens(name, T):
     check_rows(cfg, L, x, res, np.arange(T), cache={})
 
 
+@pytest.mark.parametrize("T", [1, 33, 300, 4096])
+def test_forward_fp8_activations_all_tokens(T):
+    # fp8 weights and fp8 activations at the small shape: the small-M path
+    # (dequantized bf16 rows), the mixed regime and the large-M fp8-MFMA path.
+    cfg, L = layer("small", wdtype="fp8a8")
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    res = run_forward(cfg, L, x)
+    check_routing_consistent(cfg, L, x, res)
+    check_rows(cfg, L, x, res, np.arange(T), cache={})
+
+
 @pytest.mark.parametrize("d,inter,T", [(96, 160, 1500), (160, 96, 1500), (1056, 544, 700)])
 def test_forward_k_odd_multiple_of_32(d, inter, T):
     # d or I an odd multiple of 32: the large-M kernel's last k stage holds
@@ -80,7 +91,8 @@ def _sample(x, n, extra_large=0):
 
 
 @pytest.mark.parametrize("name,n_sample,n_skew", [("decode", 8, 0), ("prefill", 6, 2),
-                                                  ("fp8", 5, 0), ("prefill32k", 4, 0)])
+                                                  ("fp8", 5, 0), ("fp8a8", 5, 0),
+                                                  ("prefill32k", 4, 0)])
 def test_forward_longcat_shape_sampled(name, n_sample, n_skew):
     cfg, L = layer(name)
     x = inputs.make_tokens(cfg, "cuda")
