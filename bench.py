@@ -66,6 +66,10 @@ def stage_of_kernel(name):
         return "gateup_large" if "<true" in name else "down_large"
     if "gemm_small" in name:
         return "gateup_small" if "<true" in name else "down_small"
+    if "quant_rows" in name:  # fp8 activations: x in the permute stage, H before down_small
+        return "quant (fp8 activations)"
+    if "stats_partial" in name or "stats_final" in name:
+        return "router statistics (outside the layer step)"
     for key, stage in (("router_gemm", "router"), ("topk", "topk"), ("combine", "combine"),
                        ("hist_kernel", "permute"), ("colscan", "permute"),
                        ("schedule_kernel", "permute"), ("scatter", "permute")):
