@@ -149,7 +149,8 @@ __global__ __launch_bounds__(kFinalWaves * 64) void stats_final_kernel(
     const double* __restrict__ part, int nblocks, int T, int K, const int* __restrict__ counts,
     int N, int E, int D, double k_e, double alpha, double lambda, double* __restrict__ stats) {
 #pragma clang fp contract(off)
-  extern __shared__ double colsum[];  // D + 2 column sums
+  extern __shared__ double colsum[];  // D + 2 column sums, then D + 1 slot counts
+  long long* slots_of = reinterpret_cast<long long*>(colsum + D + 2);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ng = D + 2, gs = N / D;
   for (int j = w; j < ng; j += kFinalWaves) {
@@ -157,14 +158,20 @@ __global__ __launch_bounds__(kFinalWaves * 64) void stats_final_kernel(
     for (int b = lane; b < nblocks; b += 64) v += part[(size_t)b * ng + j];
     v = wave_sum_f64(v);
     if (lane == 0) colsum[j] = v;
+    if (j <= D) {  // slots of group j: an integer sum, exact in any order
+      const int lo = j < D ? j * gs : N, hi = j < D ? lo + gs : E;
+      long long c = 0;
+      for (int i = lo + lane; i < hi; i += 64) c += counts[i];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
+      if (lane == 0) slots_of[j] = c;
+    }
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
   double l = 0.0;  // sum_j f_j P_j in group order
   for (int j = 0; j <= D; ++j) {
-    long long slots = 0;
-    const int lo = j < D ? j * gs : N, hi = j < D ? lo + gs : E;
-    for (int i = lo; i < hi; ++i) slots += counts[i];
+    const long long slots = slots_of[j];
     double f = 0.0, P = 0.0;
     if (T > 0) {
       P = colsum[j] / (double)T;
@@ -188,7 +195,7 @@ void launch_router_stats(const float* logits, const uint16_t* x, int T, int E, i
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(stats_partial_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   stats_partial_kernel<<<kStatsBlocks, 256, lds, s>>>(logits, x, T, E, d, N, D, part);
-  stats_final_kernel<<<1, kFinalWaves * 64, (size_t)(D + 2) * sizeof(double), s>>>(
+  stats_final_kernel<<<1, kFinalWaves * 64, (size_t)(2 * D + 3) * sizeof(double), s>>>(
       part, kStatsBlocks, T, K, counts, N, E, D, k_e, alpha, lambda, stats);
 }
 
