@@ -38,4 +38,6 @@ from .lcmoe_oracle import (  # noqa: F401
     expert_groups,
     load_balance_stats,
     hidden_z_loss,
+    silu_grad,
+    layer_backward,
 )

@@ -443,3 +443,73 @@ def hidden_z_loss(h, lam):
     mx = h.max(axis=1)
     lse = mx + np.log(np.exp(h - mx[:, None]).sum(axis=1))
     return float(lam / T * np.sum(lse * lse))
+
+
+# ----------------------------------------------------------------------------
+# Backward of the layer (gradients of a scalar loss through y; the bias is
+# used for selection only and has no gradient, selection itself is piecewise
+# constant)
+# ----------------------------------------------------------------------------
+
+
+def silu_grad(a):
+    """d silu(a) / da = sigma(a) * (1 + a * (1 - sigma(a)))."""
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def layer_backward(x, w_router, bias, k, n_ffn, get_expert, dy):
+    """Gradients of <dy, y> for y = MoE(x) ("LongCat-Flash" section 2.1: the
+    sum over the K selected of N+Z experts, gates from one softmax over all
+    experts, zero experts the identity), chain rule written out, fp64:
+
+      g_tk = p_t[idx_tk], p_t = softmax(z_t), z_t = W_r x_t
+      FFN slot (e = idx_tk < N):  u = W13_e x_t, a = u[:I], c = u[I:],
+        h = silu(a) * c, v = W2_e h
+      zero slot: v = x_t;   y_t = sum_k g_tk v_tk
+
+      dg_tk = <dy_t, v_tk>;  dv = g_tk dy_t
+      FFN: dh = W2_e^T dv;  dW2_e += dv h^T;  da = dh * c * silu'(a);
+           dc = dh * silu(a);  du = [da; dc];  dW13_e += du x_t^T;
+           dx_t += W13_e^T du
+      zero: dx_t += dv
+      router: dp_t[i] = sum_k dg_tk [i = idx_tk];  dz_t = p_t * (dp_t - <dp_t, p_t>);
+              dW_r += dz_t x_t^T;  dx_t += W_r^T dz_t
+
+    Returns dict(dx [T,d], dw_router [E,d], dw13 {e: [2I,d]}, dw2 {e: [d,I]},
+    routing) with weight gradients for the touched FFN experts only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    w_router = np.asarray(w_router, dtype=np.float64)
+    r = route(x, w_router, bias, k)
+    idx, g, p = r["idx"], r["g"], r["p"]
+    T, d = x.shape
+    dx = np.zeros_like(x)
+    dg = np.zeros(idx.shape)
+    dw13, dw2 = {}, {}
+    for e in np.unique(idx[idx < n_ffn]):
+        rows, ks = np.nonzero(idx == e)
+        w13_e, w2_e = (np.asarray(w, dtype=np.float64) for w in get_expert(int(e)))
+        inter = w2_e.shape[1]
+        xe = x[rows]
+        u = xe @ w13_e.T
+        a, c = u[:, :inter], u[:, inter:]
+        h = silu(a) * c
+        v = h @ w2_e.T
+        dg[rows, ks] = np.sum(dy[rows] * v, axis=1)
+        dv = g[rows, ks][:, None] * dy[rows]
+        dh = dv @ w2_e
+        dw2[int(e)] = dv.T @ h
+        du = np.concatenate([dh * c * silu_grad(a), dh * silu(a)], axis=1)
+        dw13[int(e)] = du.T @ xe
+        np.add.at(dx, rows, du @ w13_e)
+    zr, zk = np.nonzero(idx >= n_ffn)
+    dg[zr, zk] = np.sum(dy[zr] * x[zr], axis=1)
+    np.add.at(dx, zr, g[zr, zk][:, None] * dy[zr])
+    dp = np.zeros_like(p)
+    np.add.at(dp, (np.repeat(np.arange(T), idx.shape[1]), idx.ravel()), dg.ravel())
+    dz = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+    dx += dz @ w_router
+    return dict(dx=dx, dw_router=dz.T @ x, dw13=dw13, dw2=dw2, dg=dg, dz=dz, routing=r)

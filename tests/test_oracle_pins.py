@@ -583,3 +583,91 @@ def test_a8_zero_routing_is_exact_identity():
     get = expert_getter(L, cfg)
     y = oracle.combine_given_routing(x, r["idx"], r["g"], cfg.n_ffn, get, a8=True)
     assert np.array_equal(y, r["g"].sum(1)[:, None] * x)
+
+
+# ----------------------------------------------------------------------------
+# Backward of the layer: against torch autograd (float64, CPU) and central
+# finite differences.
+# ----------------------------------------------------------------------------
+
+
+def _torch_layer_grads(x, w_router, bias, k, n_ffn, experts, dy):
+    """The layer in torch with autograd on x, W_r and the expert weights; the
+    selection (piecewise constant) is taken from the oracle's routing."""
+    X = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    Wr = torch.tensor(np.asarray(w_router, np.float64), requires_grad=True)
+    W13 = {e: torch.tensor(np.asarray(a, np.float64), requires_grad=True) for e, (a, _) in experts.items()}
+    W2 = {e: torch.tensor(np.asarray(b, np.float64), requires_grad=True) for e, (_, b) in experts.items()}
+    idx = oracle.route(x, w_router, bias, k)["idx"]
+    p = torch.softmax(X @ Wr.T, dim=1)
+    y = torch.zeros_like(X)
+    for t in range(x.shape[0]):
+        for kk in range(k):
+            e = int(idx[t, kk])
+            if e < n_ffn:
+                u = W13[e] @ X[t]
+                inter = W2[e].shape[1]
+                v = W2[e] @ (F.silu(u[:inter]) * u[inter:])
+            else:
+                v = X[t]
+            y[t] = y[t] + p[t, e] * v
+    (y * torch.tensor(dy)).sum().backward()
+    return X.grad.numpy(), Wr.grad.numpy(), {e: W13[e].grad.numpy() for e in W13}, \
+        {e: W2[e].grad.numpy() for e in W2}
+
+
+@pytest.mark.parametrize("T,seed", [(16, 0), (40, 7)])
+def test_layer_backward_matches_torch_autograd(T, seed):
+    cfg = inputs.CONFIGS["tiny"]
+    L = inputs.make_layer(cfg, "cpu")
+    x = bf16_values(inputs.make_tokens(cfg, "cpu", tokens=T))
+    wr, b = L["w_router"].numpy(), L["bias"].numpy()
+    get = expert_getter(L, cfg)
+    experts = {e: get(e) for e in range(cfg.n_ffn)}
+    dy = np.random.default_rng(seed).normal(size=x.shape)
+    got = oracle.layer_backward(x, wr, b, cfg.k, cfg.n_ffn, get, dy)
+    dx, dwr, dw13, dw2 = _torch_layer_grads(x, wr, b, cfg.k, cfg.n_ffn, experts, dy)
+    assert np.allclose(got["dx"], dx, rtol=1e-10, atol=1e-12)
+    assert np.allclose(got["dw_router"], dwr, rtol=1e-10, atol=1e-12)
+    for e in range(cfg.n_ffn):
+        if e in got["dw13"]:
+            assert np.allclose(got["dw13"][e], dw13[e], rtol=1e-10, atol=1e-12)
+            assert np.allclose(got["dw2"][e], dw2[e], rtol=1e-10, atol=1e-12)
+        else:  # untouched expert: zero gradient
+            assert not dw13[e].any() and not dw2[e].any()
+
+
+def test_layer_backward_finite_differences():
+    cfg = inputs.CONFIGS["tiny"]
+    L = inputs.make_layer(cfg, "cpu")
+    x = bf16_values(inputs.make_tokens(cfg, "cpu", tokens=6))
+    wr, b = L["w_router"].numpy().astype(np.float64), L["bias"].numpy()
+    get = expert_getter(L, cfg)
+    dy = np.random.default_rng(3).normal(size=x.shape)
+    got = oracle.layer_backward(x, wr, b, cfg.k, cfg.n_ffn, get, dy)
+    idx0 = got["routing"]["idx"]
+
+    def loss(xx, ww):
+        # the same selection as at x (piecewise-constant selection held fixed)
+        r = oracle.route(xx, ww, b, cfg.k)
+        assert np.array_equal(r["idx"], idx0)
+        y = oracle.combine_given_routing(xx, r["idx"], r["g"], cfg.n_ffn, get)
+        return float(np.sum(dy * y))
+
+    eps = 1e-6
+    rng = np.random.default_rng(4)
+    for _ in range(6):
+        t, c = rng.integers(6), rng.integers(cfg.d)
+        e1 = np.zeros_like(x); e1[t, c] = eps
+        fd = (loss(x + e1, wr) - loss(x - e1, wr)) / (2 * eps)
+        assert math.isclose(fd, got["dx"][t, c], rel_tol=1e-5, abs_tol=1e-7)
+        i, c2 = rng.integers(cfg.n_experts), rng.integers(cfg.d)
+        e2 = np.zeros_like(wr); e2[i, c2] = eps
+        fd = (loss(x, wr + e2) - loss(x, wr - e2)) / (2 * eps)
+        assert math.isclose(fd, got["dw_router"][i, c2], rel_tol=1e-5, abs_tol=1e-7)
+
+
+def test_silu_grad_matches_autograd():
+    a = torch.linspace(-30, 30, 1001, dtype=torch.float64, requires_grad=True)
+    F.silu(a).sum().backward()
+    assert np.allclose(oracle.silu_grad(a.detach().numpy()), a.grad.numpy(), rtol=1e-13, atol=1e-15)
