@@ -324,6 +324,94 @@ def measure(cfg, steps, warmup, hip):
     return res, (L, x, out)
 
 
+def backward_work(cfg, counts, T):
+    """Algorithmic bytes and flops of each backward stage (bf16 operands,
+    fp32 slot-row intermediates): per FFN slot the operand rows are read once
+    and the results written once, each touched expert's weights are read
+    once per GEMM that uses them, and every expert's weight gradient is
+    written (zeros for an untouched expert)."""
+    N, d, I, E = cfg.n_ffn, cfg.d, cfg.inter, cfg.n_experts
+    c = counts[:N].astype(np.int64)
+    S, et = int(c.sum()), int((c > 0).sum())
+    w13, w2 = 2 * I * d * 2, d * I * 2
+    return {
+        "u": dict(bytes=et * w13 + S * (d * 2 + 2 * I * 4), flops=2.0 * S * 2 * I * d),
+        "w2t_dy": dict(bytes=et * w2 + S * (d * 2 + I * 4), flops=2.0 * S * I * d),
+        "rows_router": dict(bytes=S * (2 * I * 4 + I * 4 + 2 * I * 2 + I * 2) + 2 * T * E * 4,
+                            flops=0.0),
+        "dx_rows": dict(bytes=et * w13 + S * (2 * I * 2 + d * 4), flops=2.0 * S * 2 * I * d),
+        "dw2": dict(bytes=N * w2 + S * (d * 2 + I * 2), flops=2.0 * S * d * I),
+        "dw13": dict(bytes=N * w13 + S * (2 * I * 2 + d * 2), flops=2.0 * S * 2 * I * d),
+        "router_grads": dict(bytes=T * E * 4 + T * d * 2 + 2 * E * d * 4 + T * d * 4,
+                             flops=4.0 * T * E * d),
+        "dx": dict(bytes=S * d * 4 + T * d * (2 + 4 + 4), flops=0.0),
+    }
+
+
+def measure_backward(cfg, L, x, steps, warmup, hip):
+    """The layer backward (gradients of <dy, y> for x, W_r, W13, W2) on the
+    same layer and batch, dy ~ N(0, 1) in bf16, timed per stage."""
+    import torch
+    from mixture_experts_layer_biased_amd import inputs, lcmoe
+
+    shape = lcmoe.shape_of(cfg)
+    T = x.shape[0]
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=T)
+    ws = torch.empty(lcmoe.backward_workspace_bytes(shape, T), dtype=torch.uint8, device="cuda")
+    out = dict(dx=torch.empty(T, cfg.d, dtype=torch.float32, device="cuda"),
+               dw_router=torch.empty(cfg.n_experts, cfg.d, dtype=torch.float32, device="cuda"),
+               dw13=torch.empty(cfg.n_ffn, 2 * cfg.inter, cfg.d, dtype=torch.bfloat16,
+                                device="cuda"),
+               dw2=torch.empty(cfg.n_ffn, cfg.d, cfg.inter, dtype=torch.bfloat16, device="cuda"))
+    nst = len(lcmoe.BWD_STAGES)
+    sets = make_event_sets(hip, steps, nst + 1)
+
+    def step(ev=None):
+        lcmoe.backward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"], dy, ws=ws, out=out,
+                       stage_events=ev)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(steps):
+        step(sets[s])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per_stage = stage_ms(hip, sets, nst)
+    for arr in sets:
+        for i in range(nst + 1):
+            hip.hipEventDestroy(arr[i])
+    counts = lcmoe.route(shape, x, L["w_router"], L["bias"])["counts"].cpu().numpy()
+    work = backward_work(cfg, counts, T)
+    stages = {name: float(per_stage[i]) for i, name in enumerate(lcmoe.BWD_STAGES)}
+    roof = {}
+    for k, w in work.items():
+        sec = stages[k] / 1e3
+        roof[k] = dict(ms=stages[k], hbm_frac=w["bytes"] / sec / PEAK_HBM,
+                       mfma_frac=w["flops"] / sec / PEAK_BF16)
+    dom = max(work, key=lambda k: stages[k])
+    w = work[dom]
+    sec = stages[dom] / 1e3
+    bound = "hbm" if w["flops"] / w["bytes"] < PEAK_BF16 / PEAK_HBM else "mfma"
+    if bound == "hbm":
+        ach, peak, unit = w["bytes"] / sec / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        ach, peak, unit = w["flops"] / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
+    flops = sum(v["flops"] for v in work.values())
+    del ws, out, dy
+    torch.cuda.empty_cache()
+    return dict(tokens=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), stages_ms=stages,
+                stage_roofline=roof, dominant_kernel=dom,
+                roofline=dict(bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
+                              algorithmic_bytes=w["bytes"], flops=w["flops"],
+                              kernel_ms=stages[dom]),
+                mfma_frac=flops / (ms / 1e3) / PEAK_BF16)
+
+
 def copy_bandwidth(nbytes=4 << 30, reps=5):
     """Achievable HBM bandwidth of a plain device-to-device copy (read + write
     bytes per second), for reference next to the 8 TB/s peak."""
@@ -389,6 +477,8 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "fp8", "fp8a8", "prefill32k"], default=None,
                     help="measure a single configuration (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward measurement on the bf16 prefill batch")
     ap.add_argument("--cpu-experts", type=int, default=160)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="fold rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
@@ -428,6 +518,13 @@ def main():
               f"{res['router_stats']['ms']:.3f} ms", file=sys.stderr, flush=True)
         if name == names[0] and not args.no_cpu_baseline:
             baseline = cpu_baseline(cfg, keep[0], keep[1], keep[2], args.cpu_experts)
+        if name == "prefill" and not args.no_backward:
+            res["backward"] = measure_backward(cfg, keep[0], keep[1], args.steps, args.warmup,
+                                               hip)
+            bw = res["backward"]
+            print(f"[bench] {name} backward: {bw['ms_per_step']:.3f} ms/step, dominant "
+                  f"{bw['dominant_kernel']} {bw['roofline']['frac']:.3f} of "
+                  f"{bw['roofline']['bound']}", file=sys.stderr, flush=True)
         del keep
         torch.cuda.empty_cache()
 
@@ -456,6 +553,9 @@ def main():
                                                      "frac", "traffic")},
         "dominant_kernel": m["dominant_kernel"],
         "cpu_baseline": baseline,
+        "backward": ({k: results["prefill"]["backward"][k] for k in
+                      ("tokens", "ms_per_step", "tokens_per_s", "dominant_kernel", "roofline")}
+                     if "backward" in results.get("prefill", {}) else None),
         "copy_gbps": copy_gbps,
         "detail": results,
     }

@@ -208,6 +208,45 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
                                const int32_t* counts, double mu, double k_e,
                                float* bias, hipStream_t stream);
 
+/* Backward of the layer ("LongCat-Flash" section 2.1: y_t = sum over the K
+ * selected of the N+Z experts of g_i E_i(x_t), g from one softmax over all
+ * experts, a zero expert the identity): the gradients of <dy, y> with respect
+ * to x, W_r and the expert weights. The selection is piecewise constant and
+ * the expert bias enters it only, so neither has a gradient. Chain rule:
+ *   dg_tk = <dy_t, v_tk>;  FFN slot: dh = g W2^T dy_t, du = [dh c silu'(a);
+ *   dh silu(a)] (u = W13 x_t = [a; c]), dW2 += g dy_t h^T, dW13 += du x_t^T,
+ *   dx_t += W13^T du;  zero slot: dx_t += g dy_t;
+ *   dz_t = p_t (dp_t - <dp_t, p_t>) with dp_t[idx_tk] = dg_tk;
+ *   dW_r = dz^T x;  dx_t += W_r^T dz_t.
+ * The routing and the expert pre-activations u are recomputed from x (the
+ * same kernels as the forward, so the same selection). bf16 weights only.
+ * Expert GEMMs: bf16 operands (u and W2^T dy kept in fp32, du and g h
+ * rounded to bf16), fp32 accumulation; router gradients in fp32.
+ *
+ *   x_bf16, w_router, bias, w13, w2   as for lcmoe_forward (read)
+ *   dy_bf16    [T][d] bf16 device, read: gradient of the loss w.r.t. y
+ *   dx         [T][d] fp32 device, written
+ *   dw_router  [E][d] fp32 device, written
+ *   dw13       [N][2I][d] bf16 device, written (zero for untouched experts)
+ *   dw2        [N][d][I] bf16 device, written (zero for untouched experts)
+ *   ws         >= lcmoe_backward_workspace_bytes(shape, T) bytes
+ * Errors as lcmoe_forward; UNSUPPORTED for fp8 weights. T = 0 zeroes the
+ * weight gradients. */
+size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens);
+lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                            const float* w_router, const float* bias, const void* w13,
+                            const void* w2, const void* dy_bf16, float* dx, float* dw_router,
+                            void* dw13, void* dw2, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+/* The same call, recording the caller's 10 events (array, may be NULL) at
+ * stage boundaries: start, routing, u, W2^T dy, per-row/router, dx rows,
+ * dW2, dW13, router gradients, dx. */
+lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias, const void* w13,
+                                   const void* w2, const void* dy_bf16, float* dx,
+                                   float* dw_router, void* dw13, void* dw2, void* ws,
+                                   size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events);
+
 /* Router-side statistics ("LongCat-Flash" section 2.1, load-balance control:
  * the device-level load-balance loss L_LB = alpha * sum_{j=1..D+1} f_j P_j
  * with the zero-computation experts as group D+1; the training-stability

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblcmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["lcmoe.hip", "route.hip", "gemm.hip", "combine.hip", "stats.hip", "quant.hip"]
+SOURCES = ["lcmoe.hip", "route.hip", "gemm.hip", "combine.hip", "stats.hip", "quant.hip", "bwd_gemm.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

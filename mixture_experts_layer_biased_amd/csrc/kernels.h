@@ -63,6 +63,47 @@ void launch_combine(const uint16_t* x, const uint16_t* Y, const int* idx, const 
 void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, double k_e,
                         float* bias, hipStream_t s);
 
+// Backward grouped GEMMs: C_e[m][n] = sum_k A_e(m, k) B_e(n, k) per FFN
+// expert (see bwd_gemm.hip for the operand views).
+constexpr int kBwdRowWeight = 0;  // row of the expert's weight matrix
+constexpr int kBwdRowSlot = 1;    // slot row offsets[e] + r
+constexpr int kBwdRowToken = 2;   // token of slot row: perm[offsets[e] + r] / K
+struct BwdGemmArgs {
+  const uint16_t* a;       // A operand base (bf16)
+  long long a_ld;          // row stride (elements)
+  long long a_estride;     // per-expert element offset (weight rows)
+  int a_rows;              // kBwdRow* for A's rows
+  const uint16_t* b;
+  long long b_ld;
+  long long b_estride;
+  int b_rows;
+  void* c;                 // output, fp32 or bf16
+  long long c_ld;
+  int M, N, K;             // fixed extents (M unused when m_is_slots, K when not)
+  int m_is_slots;          // 1: M = expert's slot count, output rows are slot rows;
+                           // 0: K = slot count, output rows e * M + m
+  const int* counts;
+  const int* offsets;
+  const int* perm;
+  const int* tile_prefix;  // [N+1] prefix of ceil(count / 128) (m_is_slots)
+  int topk;
+  int n_ffn;
+};
+void launch_bwd_gemm(const BwdGemmArgs& g, bool a_ic, bool b_ic, bool out_f32, int grid,
+                     hipStream_t s);
+void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, hipStream_t s);
+void launch_bwd_rows(const float* U, const float* Q, const int* perm, const float* gate,
+                     const int* s_dev, int I, uint16_t* dU, uint16_t* Hg, float* dg, int grid,
+                     hipStream_t s);
+void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, int T, int d, int K,
+                        int N, float* dg, hipStream_t s);
+void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate, const float* dg,
+                          int T, int E, int K, float* dz, hipStream_t s);
+void launch_router_grads(const float* dz, const uint16_t* x, const float* wr, int T, int E, int d,
+                         float* dwr, float* dxr, hipStream_t s);
+void launch_bwd_dx(const float* dXs, const uint16_t* dy, const float* dxr, const int* row_of_slot,
+                   const float* gate, int T, int d, int K, float* dx, hipStream_t s);
+
 // Router-side statistics: kStatsBlocks partial rows of D+2 doubles in `part`.
 constexpr int kStatsBlocks = 1024;
 void launch_router_stats(const float* logits, const uint16_t* x, int T, int E, int d, int N, int D,

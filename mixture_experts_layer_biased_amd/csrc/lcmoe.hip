@@ -95,6 +95,42 @@ Layout make_layout(const lcmoe_shape& s, int T) {
   return L;
 }
 
+// Backward workspace: the routing and permutation regions of the forward
+// layout, then the backward's own buffers (S = T * min(K, N) slot rows).
+struct BwdLayout {
+  Layout f;
+  size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, U = 0, Q = 0, dU = 0, Hg = 0,
+         dXs = 0, dg = 0, dz = 0, dxr = 0, total = 0;
+};
+
+BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
+  BwdLayout B;
+  B.f = make_layout(s, T);
+  const long long E = n_experts(s), K = s.top_k, N = s.n_ffn, d = s.d_model, I = s.d_expert;
+  const long long S = B.f.smax;
+  size_t off = B.f.permute_end;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + kAlign - 1) / kAlign * kAlign;
+    return o;
+  };
+  B.idx = take((size_t)T * K * 4);
+  B.gate = take((size_t)T * K * 4);
+  B.counts = take((size_t)E * 4);
+  B.logits = take((size_t)T * E * 4);
+  B.tprefix = take((size_t)(N + 1) * 4);
+  B.U = take((size_t)S * 2 * I * 4);
+  B.Q = take((size_t)S * I * 4);
+  B.dU = take((size_t)S * 2 * I * 2);
+  B.Hg = take((size_t)S * I * 2);
+  B.dXs = take((size_t)S * d * 4);
+  B.dg = take((size_t)T * K * 4);
+  B.dz = take((size_t)T * E * 4);
+  B.dxr = take((size_t)T * d * 4);
+  B.total = off;
+  return B;
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Carve the workspace: returns the aligned base or nullptr if too small.
@@ -348,6 +384,155 @@ lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T, const void* x_bf
                            void* ws, size_t ws_bytes, hipStream_t stream) {
   return lcmoe_forward_staged(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale,
                               y_bf16, topk_idx, topk_gate, counts, ws, ws_bytes, stream, nullptr);
+}
+
+size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens) {
+  if (check_shape(shape) != LCMOE_OK || max_tokens < 0 || shape->w_dtype != LCMOE_W_BF16) return 0;
+  if ((long long)max_tokens * shape->top_k >= (1ll << 31)) return 0;
+  size_t best = make_bwd_layout(*shape, max_tokens).total;
+  const int lim = std::min<int>(max_tokens, 32768);
+  for (int t = 1; t <= lim; ++t) best = std::max(best, make_bwd_layout(*shape, t).total);
+  return best + kAlign;
+}
+
+lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias, const void* w13,
+                                   const void* w2, const void* dy_bf16, float* dx,
+                                   float* dw_router, void* dw13, void* dw2, void* ws,
+                                   size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (shape->w_dtype != LCMOE_W_BF16) return LCMOE_ERR_UNSUPPORTED;
+  if (T < 0 || dw_router == nullptr || dw13 == nullptr || dw2 == nullptr)
+    return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (x_bf16 == nullptr || w_router == nullptr || bias == nullptr || w13 == nullptr ||
+                w2 == nullptr || dy_bf16 == nullptr || dx == nullptr))
+    return LCMOE_ERR_INVALID_ARG;
+  if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
+  const int N = shape->n_ffn, d = shape->d_model, I = shape->d_expert, K = shape->top_k;
+  const int E = (int)n_experts(*shape);
+  if (T == 0) {  // no tokens: every gradient is zero
+    if (hipMemsetAsync(dw_router, 0, (size_t)E * d * 4, stream) != hipSuccess ||
+        hipMemsetAsync(dw13, 0, (size_t)N * 2 * I * d * 2, stream) != hipSuccess ||
+        hipMemsetAsync(dw2, 0, (size_t)N * d * I * 2, stream) != hipSuccess)
+      return LCMOE_ERR_HIP;
+    return LCMOE_OK;
+  }
+  if (!aligned16(x_bf16) || !aligned16(w_router) || !aligned16(w13) || !aligned16(w2) ||
+      !aligned16(dy_bf16) || !aligned16(dx) || !aligned16(dw_router) || !aligned16(dw13) ||
+      !aligned16(dw2))
+    return LCMOE_ERR_UNSUPPORTED;
+  const BwdLayout B = make_bwd_layout(*shape, T);
+  const Layout& L = B.f;
+  char* base = ws_base(ws, ws_bytes, B.total);
+  if (base == nullptr) return LCMOE_ERR_WORKSPACE;
+  clear_hip_error();
+
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const uint16_t* dy = static_cast<const uint16_t*>(dy_bf16);
+  int* idx = at<int>(base, B.idx);
+  float* gate = at<float>(base, B.gate);
+  int* counts = at<int>(base, B.counts);
+  float* logits = at<float>(base, B.logits);
+  int* offsets = at<int>(base, L.offsets);
+  int* perm = at<int>(base, L.perm);
+  int* row_of_slot = at<int>(base, L.row_of_slot);
+  int* tprefix = at<int>(base, B.tprefix);
+  float* U = at<float>(base, B.U);
+  float* Q = at<float>(base, B.Q);
+  uint16_t* dU = at<uint16_t>(base, B.dU);
+  uint16_t* Hg = at<uint16_t>(base, B.Hg);
+  float* dXs = at<float>(base, B.dXs);
+  float* dg = at<float>(base, B.dg);
+  float* dz = at<float>(base, B.dz);
+  float* dxr = at<float>(base, B.dxr);
+
+  // 1. routing as in the forward (same kernels, so the same selection), with
+  //    the fp32 logits kept for the softmax backward, and the permutation
+  mark(ev, 0, stream);
+  launch_router(x, w_router, at<float>(base, L.zpart), T, E, d, L.ks, L.kchunk, stream);
+  launch_topk(at<float>(base, L.zpart), L.ks, bias, T, E, K, idx, gate, logits, stream);
+  launch_permute(idx, T, K, E, N, L.ntile, at<unsigned long long>(base, L.masks),
+                 at<int>(base, L.tilecnt), at<int>(base, L.tileoff), counts, offsets,
+                 at<int>(base, L.small_list), at<int>(base, L.mt_prefix), at<int>(base, L.meta),
+                 perm, row_of_slot, stream);
+  launch_tile_prefix(counts, N, 128, tprefix, stream);
+  mark(ev, 1, stream);
+
+  const long long smax = L.smax;
+  auto slot_grid = [&](int n) {  // upper bound of (m tiles over all experts) x (n tiles)
+    return (int)std::min<long long>((smax / 128 + N) * ((n + 127) / 128), 1ll << 30);
+  };
+  BwdGemmArgs g{};
+  g.counts = counts;
+  g.offsets = offsets;
+  g.perm = perm;
+  g.tile_prefix = tprefix;
+  g.topk = K;
+  g.n_ffn = N;
+
+  // 2. U = X_e W13_e^T (pre-activations, fp32), per FFN slot row
+  g.a = x; g.a_ld = d; g.a_estride = 0; g.a_rows = kBwdRowToken;
+  g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
+  g.b_rows = kBwdRowWeight;
+  g.c = U; g.c_ld = 2 * I; g.N = 2 * I; g.K = d; g.m_is_slots = 1;
+  launch_bwd_gemm(g, false, false, true, slot_grid(2 * I), stream);
+  mark(ev, 2, stream);
+
+  // 3. Q = dY_e W2_e (W2 read k-major), per FFN slot row
+  g.a = dy; g.a_ld = d; g.a_rows = kBwdRowToken;
+  g.b = static_cast<const uint16_t*>(w2); g.b_ld = I; g.b_estride = (long long)d * I;
+  g.b_rows = kBwdRowWeight;
+  g.c = Q; g.c_ld = I; g.N = I; g.K = d; g.m_is_slots = 1;
+  launch_bwd_gemm(g, false, true, true, slot_grid(I), stream);
+  mark(ev, 3, stream);
+
+  // 4. per slot row: dg, dU, g*h; zero-slot dg; router dz
+  launch_bwd_rows(U, Q, perm, gate, at<int>(base, L.meta) + 2, I, dU, Hg, dg,
+                  (int)std::min<long long>(4096, (smax + 3) / 4), stream);
+  launch_bwd_zero_dg(x, dy, idx, T, d, K, N, dg, stream);
+  launch_bwd_router_dz(logits, idx, gate, dg, T, E, K, dz, stream);
+  mark(ev, 4, stream);
+
+  // 5. dX per slot row = dU_e W13_e (W13 read k-major)
+  g.a = dU; g.a_ld = 2 * I; g.a_rows = kBwdRowSlot;
+  g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
+  g.b_rows = kBwdRowWeight;
+  g.c = dXs; g.c_ld = d; g.N = d; g.K = 2 * I; g.m_is_slots = 1;
+  launch_bwd_gemm(g, false, true, true, slot_grid(d), stream);
+  mark(ev, 5, stream);
+
+  // 6. dW2_e[c][j] = sum over the expert's slots of dy[t][c] (g h)[s][j]
+  g.a = dy; g.a_ld = d; g.a_rows = kBwdRowToken;
+  g.b = Hg; g.b_ld = I; g.b_estride = 0; g.b_rows = kBwdRowSlot;
+  g.c = dw2; g.c_ld = I; g.M = d; g.N = I; g.m_is_slots = 0;
+  launch_bwd_gemm(g, true, true, false, N * ((d + 127) / 128) * ((I + 127) / 128), stream);
+  mark(ev, 6, stream);
+
+  // 7. dW13_e[r][c] = sum over the expert's slots of dU[s][r] x[t][c]
+  g.a = dU; g.a_ld = 2 * I; g.a_rows = kBwdRowSlot;
+  g.b = x; g.b_ld = d; g.b_rows = kBwdRowToken;
+  g.c = dw13; g.c_ld = d; g.M = 2 * I; g.N = d; g.m_is_slots = 0;
+  launch_bwd_gemm(g, true, true, false, N * ((2 * I + 127) / 128) * ((d + 127) / 128), stream);
+  mark(ev, 7, stream);
+
+  // 8. router: dW_r = dz^T x, dx_r = dz W_r (fp32)
+  launch_router_grads(dz, x, w_router, T, E, d, dw_router, dxr, stream);
+  mark(ev, 8, stream);
+
+  // 9. dx
+  launch_bwd_dx(dXs, dy, dxr, row_of_slot, gate, T, d, K, dx, stream);
+  mark(ev, 9, stream);
+  return hip_status();
+}
+
+lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                            const float* w_router, const float* bias, const void* w13,
+                            const void* w2, const void* dy_bf16, float* dx, float* dw_router,
+                            void* dw13, void* dw2, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return lcmoe_backward_staged(shape, T, x_bf16, w_router, bias, w13, w2, dy_bf16, dx, dw_router,
+                               dw13, dw2, ws, ws_bytes, stream, nullptr);
 }
 
 lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all, const int32_t* counts,

@@ -10,7 +10,7 @@ section 1 table: d_model 6144, 512 FFN experts, 256 zero-computation experts,
 12 experts per token, expert intermediate size 2048; plus a tiny and a small
 layer of the same structure. Every tensor has its own generator stream,
 seeded seed*1000 + stream id (x 0, W_r 1, W13 2, W2 3, bias 4, skew subset 5,
-bias-loop batch j 100+j).
+bias-loop batch j 100+j, upstream gradient dy 7).
 """
 
 from dataclasses import dataclass, field, replace
@@ -89,6 +89,15 @@ def make_tokens(cfg, device, stream=0, tokens=None, skew=True):
         sel = torch.randperm(T, generator=gs, device=device)[:n_skew]
         x[sel] *= cfg.skew_factor
     return x.to(torch.bfloat16)
+
+
+def make_upstream_grad(cfg, device, tokens=None):
+    """dy: bf16 [T, d] ~ N(0, 1), the gradient arriving at the layer output
+    (its own stream, independent of the tokens)."""
+    T = cfg.tokens if tokens is None else tokens
+    g = _gen(device, cfg.seed, 7)
+    return torch.randn(T, cfg.d, generator=g, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)
 
 
 def quantize_fp8_blocks(w):

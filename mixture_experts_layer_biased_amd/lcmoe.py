@@ -18,7 +18,8 @@ W_BF16, W_FP8_E4M3_B128, W_FP8_E4M3_B128_A8 = 0, 1, 2
 
 EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
            "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
-           "lcmoe_router_stats", "lcmoe_status_str")
+           "lcmoe_router_stats", "lcmoe_backward_workspace_bytes", "lcmoe_backward",
+           "lcmoe_backward_staged", "lcmoe_status_str")
 NUM_STAGES = 8
 STAGES = ("router", "topk", "permute", "gateup_small", "gateup_large", "down_small",
           "down_large", "combine")
@@ -84,6 +85,12 @@ def lib():
     L.lcmoe_router_stats.argtypes = [S, i32, _P, _P, _P, i32, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_double, _P, _P, sz, _P]
     L.lcmoe_router_stats.restype = st
+    L.lcmoe_backward_workspace_bytes.argtypes = [S, i32]
+    L.lcmoe_backward_workspace_bytes.restype = sz
+    L.lcmoe_backward.argtypes = [S, i32] + [_P] * 11 + [sz, _P]
+    L.lcmoe_backward.restype = st
+    L.lcmoe_backward_staged.argtypes = [S, i32] + [_P] * 11 + [sz, _P, _P]
+    L.lcmoe_backward_staged.restype = st
     L.lcmoe_status_str.argtypes = [st]
     L.lcmoe_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -226,3 +233,38 @@ def router_stats(shape, x, logits, counts, n_groups, k_e, alpha=1.0, lam=1.0, ws
                                     _ptr(stats), _ptr(ws), ws.numel(), _stream()),
            "lcmoe_router_stats")
     return stats
+
+
+NUM_BWD_STAGES = 9
+BWD_STAGES = ("routing", "u", "w2t_dy", "rows_router", "dx_rows", "dw2", "dw13", "router_grads",
+              "dx")
+
+
+def backward_workspace_bytes(shape, max_tokens):
+    return int(lib().lcmoe_backward_workspace_bytes(ctypes.byref(shape), int(max_tokens)))
+
+
+def backward(shape, x, w_router, bias, w13, w2, dy, ws=None, out=None, stage_events=None):
+    """Gradients of <dy, y> for y = forward(...). Returns dict(dx fp32 [T,d],
+    dw_router fp32 [E,d], dw13 bf16 [N,2I,d], dw2 bf16 [N,d,I])."""
+    T, d = x.shape
+    dev = x.device
+    E, N, I = shape.n_experts, shape.n_ffn, shape.d_expert
+    o = out or {}
+    dx = o.get("dx", torch.empty(T, d, dtype=torch.float32, device=dev))
+    dwr = o.get("dw_router", torch.empty(E, d, dtype=torch.float32, device=dev))
+    dw13 = o.get("dw13", torch.empty(N, 2 * I, d, dtype=torch.bfloat16, device=dev))
+    dw2 = o.get("dw2", torch.empty(N, d, I, dtype=torch.bfloat16, device=dev))
+    if ws is None:
+        n = backward_workspace_bytes(shape, T)
+        if n == 0:
+            raise LcmoeError(ERR_INVALID_ARG, "invalid or unsupported shape")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    _dev(x, w_router, bias, w13, w2, dy, dx, dwr, dw13, dw2, ws)
+    args = (ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13), _ptr(w2),
+            _ptr(dy), _ptr(dx), _ptr(dwr), _ptr(dw13), _ptr(dw2), _ptr(ws), ws.numel(), _stream())
+    if stage_events is None:
+        _check(lib().lcmoe_backward(*args), "lcmoe_backward")
+    else:
+        _check(lib().lcmoe_backward_staged(*args, stage_events), "lcmoe_backward_staged")
+    return dict(dx=dx, dw_router=dwr, dw13=dw13, dw2=dw2)

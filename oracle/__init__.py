@@ -39,5 +39,6 @@ from .lcmoe_oracle import (  # noqa: F401
     load_balance_stats,
     hidden_z_loss,
     silu_grad,
+    expert_backward,
     layer_backward,
 )

@@ -459,7 +459,28 @@ def silu_grad(a):
     return s * (1.0 + a * (1.0 - s))
 
 
-def layer_backward(x, w_router, bias, k, n_ffn, get_expert, dy):
+def expert_backward(x_rows, g, dy_rows, w13, w2):
+    """One FFN expert's part of the backward (see layer_backward): for its
+    rows x_rows [m, d] with gates g [m] and upstream gradients dy_rows [m, d],
+    returns (dx_rows [m, d], dw13 [2I, d], dw2 [d, I], dg [m]), fp64."""
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    dy_rows = np.asarray(dy_rows, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    w13 = np.asarray(w13, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    inter = w2.shape[1]
+    u = x_rows @ w13.T
+    a, c = u[:, :inter], u[:, inter:]
+    h = silu(a) * c
+    v = h @ w2.T
+    dg = np.sum(dy_rows * v, axis=1)
+    dv = g[:, None] * dy_rows
+    dh = dv @ w2
+    du = np.concatenate([dh * c * silu_grad(a), dh * silu(a)], axis=1)
+    return du @ w13, du.T @ x_rows, dv.T @ h, dg
+
+
+def layer_backward(x, w_router, bias, k, n_ffn, get_expert, dy, idx=None):
     """Gradients of <dy, y> for y = MoE(x) ("LongCat-Flash" section 2.1: the
     sum over the K selected of N+Z experts, gates from one softmax over all
     experts, zero experts the identity), chain rule written out, fp64:
@@ -479,11 +500,17 @@ def layer_backward(x, w_router, bias, k, n_ffn, get_expert, dy):
 
     Returns dict(dx [T,d], dw_router [E,d], dw13 {e: [2I,d]}, dw2 {e: [d,I]},
     routing) with weight gradients for the touched FFN experts only.
+    idx: optional [T, K] selection to use instead of the oracle's own (the
+    gates are still the oracle's fp64 softmax at those experts).
     """
     x = np.asarray(x, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
     w_router = np.asarray(w_router, dtype=np.float64)
     r = route(x, w_router, bias, k)
+    if idx is not None:
+        idx = np.asarray(idx)
+        g, p = softmax_gates(r["z"], idx)
+        r = dict(r, idx=idx, g=g, p=p)
     idx, g, p = r["idx"], r["g"], r["p"]
     T, d = x.shape
     dx = np.zeros_like(x)
@@ -491,20 +518,10 @@ def layer_backward(x, w_router, bias, k, n_ffn, get_expert, dy):
     dw13, dw2 = {}, {}
     for e in np.unique(idx[idx < n_ffn]):
         rows, ks = np.nonzero(idx == e)
-        w13_e, w2_e = (np.asarray(w, dtype=np.float64) for w in get_expert(int(e)))
-        inter = w2_e.shape[1]
-        xe = x[rows]
-        u = xe @ w13_e.T
-        a, c = u[:, :inter], u[:, inter:]
-        h = silu(a) * c
-        v = h @ w2_e.T
-        dg[rows, ks] = np.sum(dy[rows] * v, axis=1)
-        dv = g[rows, ks][:, None] * dy[rows]
-        dh = dv @ w2_e
-        dw2[int(e)] = dv.T @ h
-        du = np.concatenate([dh * c * silu_grad(a), dh * silu(a)], axis=1)
-        dw13[int(e)] = du.T @ xe
-        np.add.at(dx, rows, du @ w13_e)
+        w13_e, w2_e = get_expert(int(e))
+        dxe, dw13[int(e)], dw2[int(e)], dg[rows, ks] = expert_backward(
+            x[rows], g[rows, ks], dy[rows], w13_e, w2_e)
+        np.add.at(dx, rows, dxe)
     zr, zk = np.nonzero(idx >= n_ffn)
     dg[zr, zk] = np.sum(dy[zr] * x[zr], axis=1)
     np.add.at(dx, zr, g[zr, zk][:, None] * dy[zr])

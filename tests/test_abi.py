@@ -174,3 +174,44 @@ def test_router_stats_validation():
     assert _stats(s, 4) == ERR_WORKSPACE
     assert _stats(s, 4, ws=FAKE, wsb=64) == ERR_WORKSPACE
     assert _stats(shp(n_ffn=0), 4) == ERR_INVALID_ARG
+
+
+def _backward(shape, T, x=FAKE, wr=FAKE, b=FAKE, w13=FAKE, w2=FAKE, dy=FAKE, dx=FAKE, dwr=FAKE,
+              dw13=FAKE, dw2=FAKE, ws=None, wsb=0):
+    return lcmoe.lib().lcmoe_backward(ctypes.byref(shape), T, x, wr, b, w13, w2, dy, dx, dwr,
+                                      dw13, dw2, ws, wsb, None)
+
+
+def test_backward_validation():
+    s = shp()
+    assert _backward(s, -1) == ERR_INVALID_ARG
+    for arg in ("x", "wr", "b", "w13", "w2", "dy", "dx", "dwr", "dw13", "dw2"):
+        assert _backward(s, 4, **{arg: None}) == ERR_INVALID_ARG, arg
+    for arg in ("x", "dy", "dx", "dwr", "dw13", "dw2"):
+        assert _backward(s, 4, **{arg: MIS}) == ERR_UNSUPPORTED, arg
+    assert _backward(s, 4) == ERR_WORKSPACE
+    need = lcmoe.backward_workspace_bytes(s, 4)
+    assert need > 64
+    assert _backward(s, 4, ws=FAKE, wsb=64) == ERR_WORKSPACE
+    assert _backward(s, 2 ** 31 // 3 + 1) == ERR_UNSUPPORTED   # T*K >= 2^31
+    # fp8 weights: no backward
+    for wd in (1, 2):
+        f = make_shape(128, 8, 4, 3, 128, wd)
+        assert lcmoe.backward_workspace_bytes(f, 4) == 0
+        assert _backward(f, 4) == ERR_UNSUPPORTED
+    assert lcmoe.backward_workspace_bytes(s, -1) == 0
+
+
+@pytest.mark.parametrize("dims", [(64, 8, 4, 3, 32), (6144, 512, 256, 12, 2048)])
+def test_backward_workspace(dims):
+    s = make_shape(*dims)
+    d, N, Z, K, I = dims
+    prev = 0
+    for T in [0, 1, 2, 63, 64, 65, 1000, 8192]:
+        n = lcmoe.backward_workspace_bytes(s, T)
+        assert n >= prev, (T, n, prev)
+        prev = n
+    # the fp32 slot-row intermediates U, Q, dX_s and the bf16 dU, g*h
+    S = 8192 * min(K, N)
+    assert lcmoe.backward_workspace_bytes(s, 8192) >= S * (2 * I * 4 + I * 4 + d * 4 + 2 * I * 2
+                                                           + I * 2)

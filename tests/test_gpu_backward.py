@@ -1,0 +1,225 @@
+"""GPU parity of the layer backward against the oracle.
+
+The GPU computes the gradients of <dy, y> for the layer's forward; the oracle
+(fp64) does the same on the GPU's own selection (the selection itself is
+checked bit-exact elsewhere). Tolerances, max relative error per row against
+the row's infinity norm:
+  dx, dW_r (fp32 outputs): 2e-2. The expert operands are bf16 (x, dy, the
+    weights), the slot-row intermediates dU are rounded to bf16 once before
+    the dU W13 product (unit roundoff 2^-9), the rest accumulates in fp32.
+  dW13, dW2 (bf16 outputs): 2e-2, the same rounding of dU / g*h plus one
+    bf16 rounding of the result.
+Untouched experts' weight gradients must be exactly zero.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_biased_amd import inputs, lcmoe
+from tests.gpu_common import layer, max_rel_err
+from tests.helpers import bf16_values, expert_getter
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def run_backward(cfg, L, x, dy, **kw):
+    shape = lcmoe.shape_of(cfg)
+    res = lcmoe.backward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"], dy, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def gpu_selection(cfg, L, x):
+    r = lcmoe.route(lcmoe.shape_of(cfg), x, L["w_router"], L["bias"])
+    torch.cuda.synchronize()
+    return r["idx"].cpu().numpy()
+
+
+def oracle_backward(cfg, L, x, dy, idx, cache=None):
+    get = expert_getter(L, "bf16", cache=cache)
+    return oracle.layer_backward(bf16_values(x), L["w_router"].cpu().numpy(),
+                                 L["bias"].cpu().numpy(), cfg.k, cfg.n_ffn, get,
+                                 bf16_values(dy), idx=idx)
+
+
+def untouched_are_zero(res, touched, n_ffn):
+    mask = torch.ones(n_ffn, dtype=torch.bool, device=res["dw13"].device)
+    mask[torch.as_tensor(sorted(touched), dtype=torch.long, device=mask.device)] = False
+    z13 = res["dw13"].view(n_ffn, -1)[mask].view(torch.int16).abs().amax() if mask.any() else 0
+    z2 = res["dw2"].view(n_ffn, -1)[mask].view(torch.int16).abs().amax() if mask.any() else 0
+    return int(z13) == 0 and int(z2) == 0
+
+
+def check_all(cfg, L, x, dy, res, idx, experts=None, cache=None):
+    ref = oracle_backward(cfg, L, x, dy, idx, cache=cache)
+    errs = {"dx": max_rel_err(res["dx"].cpu().numpy(), ref["dx"]),
+            "dw_router": max_rel_err(res["dw_router"].cpu().numpy(), ref["dw_router"])}
+    touched = sorted(ref["dw13"])
+    for e in touched if experts is None else [e for e in experts if e in ref["dw13"]]:
+        errs[f"dw13[{e}]"] = max_rel_err(bf16_values(res["dw13"][e]), ref["dw13"][e])
+        errs[f"dw2[{e}]"] = max_rel_err(bf16_values(res["dw2"][e]), ref["dw2"][e])
+    worst = max(errs, key=errs.get)
+    print(f"{cfg.name} T={x.shape[0]}: {len(touched)} experts touched, "
+          f"worst {worst} {errs[worst]:.3e}, dx {errs['dx']:.3e}, dW_r {errs['dw_router']:.3e}")
+    assert errs[worst] < TOL, errs
+    assert untouched_are_zero(res, touched, cfg.n_ffn)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 16), ("tiny", 777),
+                                    ("small", 33), ("small", 300), ("small", 4096)])
+def test_backward_all_tokens(name, T):
+    # T spans one token, several 128-row M tiles per expert and ragged tails
+    # in every grouped GEMM (slot rows in the dgrad GEMMs, the reduction over
+    # slots in the wgrad GEMMs).
+    cfg, L = layer(name)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=T)
+    res = run_backward(cfg, L, x, dy)
+    check_all(cfg, L, x, dy, res, gpu_selection(cfg, L, x), cache={})
+
+
+@pytest.mark.parametrize("d,inter,T", [(96, 160, 1500), (160, 96, 300)])
+def test_backward_odd_multiples_of_32(d, inter, T):
+    # d and I not multiples of the 128-wide tiles: partial N tiles and a
+    # k range ending inside a 32-wide stage.
+    cfg, L = layer("tiny", d=d, inter=inter)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=T)
+    res = run_backward(cfg, L, x, dy)
+    check_all(cfg, L, x, dy, res, gpu_selection(cfg, L, x), cache={})
+
+
+def test_backward_zero_routing_closed_form():
+    # FFN experts biased out: y_t = (sum_k g_tk) x_t, so
+    # dx_t = G_t dy_t + W_r^T dz_t and every expert weight gradient is zero.
+    cfg, L = layer("small")
+    b = L["bias"].clone()
+    b[: cfg.n_ffn] = -1e4
+    L2 = dict(L, bias=b)
+    T = 500
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=T)
+    res = run_backward(cfg, L2, x, dy)
+    idx = gpu_selection(cfg, L2, x)
+    assert np.all(idx >= cfg.n_ffn)
+    assert untouched_are_zero(res, [], cfg.n_ffn)
+    check_all(cfg, L2, x, dy, res, idx, cache={})
+
+
+def _sample(T, n):
+    return np.array(sorted(set(np.linspace(0, T - 1, n).astype(int))))
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_backward_longcat_shape(name):
+    # LongCat shape. (1) A handful of tokens on their own: every output
+    # checked (dW13/dW2 on three touched experts, the rest zero). (2) The
+    # full batch: dx on sampled tokens and dW13/dW2 of two experts against
+    # the oracle, and dW_r equal to the sum of the two half batches' dW_r.
+    cfg, L = layer(name)
+    x = inputs.make_tokens(cfg, "cuda")
+    dy = inputs.make_upstream_grad(cfg, "cuda")
+    T = x.shape[0]
+    toks = _sample(T, 4)
+    xs, dys = x[torch.as_tensor(toks, device="cuda")], dy[torch.as_tensor(toks, device="cuda")]
+    res = run_backward(cfg, L, xs, dys)
+    idx_s = gpu_selection(cfg, L, xs)
+    ffn = sorted(set(idx_s[idx_s < cfg.n_ffn].tolist()))
+    check_all(cfg, L, xs, dys, res, idx_s, experts=[ffn[0], ffn[len(ffn) // 2], ffn[-1]])
+    del res
+
+    res = run_backward(cfg, L, x, dy)
+    idx = gpu_selection(cfg, L, x)
+    # dx on sampled tokens: a token's dx depends on that token alone
+    toks = _sample(T, 6)
+    ref = oracle_backward(cfg, L, x[torch.as_tensor(toks, device="cuda")],
+                          dy[torch.as_tensor(toks, device="cuda")], idx[toks])
+    err_dx = max_rel_err(res["dx"][torch.as_tensor(toks, device="cuda")].cpu().numpy(), ref["dx"])
+    # weight gradients of the most loaded expert and of the last touched one
+    counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)[: cfg.n_ffn]
+    errs = {}
+    for e in sorted({int(np.argmax(counts)), int(np.nonzero(counts)[0][-1])}):
+        rows, ks = np.nonzero(idx == e)
+        xe = x[torch.as_tensor(rows, device="cuda")]
+        dye = dy[torch.as_tensor(rows, device="cuda")]
+        xv, dyv = bf16_values(xe), bf16_values(dye)
+        z = oracle.router_logits(xv, L["w_router"].cpu().numpy())
+        g, _ = oracle.softmax_gates(z, idx[rows])
+        w13_e, w2_e = expert_getter(L, "bf16")(e)
+        _, dw13, dw2, _ = oracle.expert_backward(xv, g[np.arange(len(rows)), ks], dyv,
+                                                 w13_e, w2_e)
+        errs[f"dw13[{e}] ({counts[e]} rows)"] = max_rel_err(bf16_values(res["dw13"][e]), dw13)
+        errs[f"dw2[{e}]"] = max_rel_err(bf16_values(res["dw2"][e]), dw2)
+    print(f"{name} T={T}: dx {err_dx:.3e} over {len(toks)} tokens; {errs}")
+    assert err_dx < TOL
+    assert max(errs.values()) < TOL, errs
+    # dW_r is a sum over tokens: full batch = first half + second half. The
+    # router's fp32 split-K summation order depends on the batch size, so a
+    # token at a near tie may be routed differently in a half batch; such
+    # tokens get dy = 0, which removes them from every gradient exactly.
+    h = T // 2
+    halves = np.concatenate([gpu_selection(cfg, L, x[:h]), gpu_selection(cfg, L, x[h:])])
+    flipped = np.nonzero((np.sort(halves, 1) != np.sort(idx, 1)).any(1))[0]
+    dy2 = dy.clone()
+    dy2[torch.as_tensor(flipped, dtype=torch.long, device="cuda")] = 0
+    out = dict(dw13=res["dw13"], dw2=res["dw2"])
+    full = run_backward(cfg, L, x, dy2, out=out)["dw_router"].double()
+    a = run_backward(cfg, L, x[:h], dy2[:h], out=out)["dw_router"].double()
+    b = run_backward(cfg, L, x[h:], dy2[h:], out=out)["dw_router"].double()
+    err_r = max_rel_err((a + b).cpu().numpy(), full.cpu().numpy())
+    print(f"{name}: dW_r additivity {err_r:.3e} ({len(flipped)} tokens routed differently "
+          f"in the half batches)")
+    assert len(flipped) <= max(2, T // 1000)
+    assert err_r < 1e-3
+
+
+def test_backward_zero_tokens_and_determinism():
+    cfg, L = layer("small")
+    shape = lcmoe.shape_of(cfg)
+    x0 = torch.empty(0, cfg.d, dtype=torch.bfloat16, device="cuda")
+    out = dict(dw_router=torch.full((cfg.n_experts, cfg.d), 7.0, device="cuda"),
+               dw13=torch.ones(cfg.n_ffn, 2 * cfg.inter, cfg.d, dtype=torch.bfloat16,
+                               device="cuda"),
+               dw2=torch.ones(cfg.n_ffn, cfg.d, cfg.inter, dtype=torch.bfloat16, device="cuda"))
+    lcmoe.backward(shape, x0, L["w_router"], L["bias"], L["w13"], L["w2"], x0, out=out)
+    torch.cuda.synchronize()
+    assert all(int(torch.count_nonzero(out[k])) == 0 for k in out)
+    x = inputs.make_tokens(cfg, "cuda", tokens=2500)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=2500)
+    a = run_backward(cfg, L, x, dy)
+    b = run_backward(cfg, L, x, dy)
+    for k in ("dx", "dw_router", "dw13", "dw2"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_backward_staged_events_and_workspace_reuse():
+    # the staged entry point gives the same gradients and records every
+    # stage; a workspace sized for a larger batch serves a smaller one.
+    cfg, L = layer("small")
+    x = inputs.make_tokens(cfg, "cuda", tokens=1000)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=1000)
+    ref = run_backward(cfg, L, x, dy)
+    ws = torch.empty(lcmoe.backward_workspace_bytes(lcmoe.shape_of(cfg), 4096),
+                     dtype=torch.uint8, device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    n = len(lcmoe.BWD_STAGES)
+    ev = (ctypes.c_void_p * (n + 1))()
+    for i in range(n + 1):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        ev[i] = h
+    got = run_backward(cfg, L, x, dy, ws=ws, stage_events=ev)
+    for k in ("dx", "dw_router", "dw13", "dw2"):
+        assert torch.equal(ref[k], got[k]), k
+    ms = ctypes.c_float()
+    for i in range(n):
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[i], ev[i + 1]) == 0
+        assert ms.value >= 0
