@@ -15,9 +15,16 @@
 //
 // Tiles of 128 x 128 x 32, 256 threads (2 x 2 waves of 64 x 64 = 2 x 2
 // fragments), register-staged double buffering: the next k stage is loaded
-// into registers while the current one is multiplied from LDS. LDS tiles
-// are [128 rows][32 k] bf16 (64-byte rows, chunk c of row r at
-// c ^ ((r >> 2) & 3)); i-contiguous operands are transposed on the way in.
+// into registers while the current one is multiplied from LDS. Both
+// operand forms are stored in LDS as they sit in memory, 16 bytes at a time:
+//   k-contiguous: [128 rows][32 k] (64-byte rows, chunk c of row r at
+//     c ^ ((r >> 2) & 3)), read with 16-byte loads;
+//   i-contiguous: [32 k][128 i] (256-byte rows, 64-byte window w of row k at
+//     w ^ (k & 3)), read with the gfx950 transposing LDS load
+//     (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one i.
+// The MFMA computes the transposed tile (B as its first operand), so each
+// lane holds 4 consecutive n of one output row: 16-byte (fp32) or 8-byte
+// (bf16) stores.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,6 +36,31 @@ constexpr int BT = 128;  // tile rows (m and n)
 constexpr int BKB = 32;  // k per stage
 
 __device__ __forceinline__ int sw64(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+
+// i-contiguous tile [32 k][128 i]: element offset of (k, i), i a multiple of 4.
+__device__ __forceinline__ int swkm(int k, int i) {
+  return k * 128 + ((((i >> 5) ^ (k & 3)) << 5) | (i & 31));
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// MFMA operand (rows base + lane % 32, k 16 ks + 8 (lane / 32) + [0, 8)) from
+// an i-contiguous tile. ds_read_b64_tr_b16 works on groups of 16 lanes: lane
+// s of a group names 4 consecutive i of one k row; the lane j of the group
+// receives, for t = 0..3, element j % 4 of the group's lane j / 4 + 4 t. With
+// lane s reading row k0 + s / 4 at i0 + 4 (s % 4), lane j gets (i0 + j,
+// k0 + t): four consecutive k of one row of the operand.
+__device__ __forceinline__ bf16x8_t km_frag(const uint16_t* tile, int base, int ks, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int i = base + 16 * (g & 1) + 4 * (s & 3);
+  const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + swkm(k, i)));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + swkm(k + 4, i)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 struct OpView {
   const uint16_t* base;
@@ -128,30 +160,12 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int q = tid + 256 * j;
-      if (!A_IC) {
-        sA[buf][sw64(q >> 2, q & 3)] = ra[j];
-      } else {
-        const int kr = q >> 4, i8 = 8 * (q & 15);
-        uint16_t* s = reinterpret_cast<uint16_t*>(sA[buf]);
-        const uint32_t w[4] = {ra[j].x, ra[j].y, ra[j].z, ra[j].w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = i8 + u;
-          s[sw64(row, kr >> 3) * 8 + (kr & 7)] = (uint16_t)(w[u >> 1] >> (16 * (u & 1)));
-        }
-      }
-      if (!B_IC) {
-        sB[buf][sw64(q >> 2, q & 3)] = rb[j];
-      } else {
-        const int kr = q >> 4, i8 = 8 * (q & 15);
-        uint16_t* s = reinterpret_cast<uint16_t*>(sB[buf]);
-        const uint32_t w[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = i8 + u;
-          s[sw64(row, kr >> 3) * 8 + (kr & 7)] = (uint16_t)(w[u >> 1] >> (16 * (u & 1)));
-        }
-      }
+      if (!A_IC) sA[buf][sw64(q >> 2, q & 3)] = ra[j];
+      else *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(sA[buf]) +
+                                     swkm(q >> 4, 8 * (q & 15))) = ra[j];
+      if (!B_IC) sB[buf][sw64(q >> 2, q & 3)] = rb[j];
+      else *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(sB[buf]) +
+                                     swkm(q >> 4, 8 * (q & 15))) = rb[j];
     }
   };
 
@@ -177,14 +191,21 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmArgs g) {
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t av[2], bv[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = as_bf16x8(sA[buf][sw64(64 * wm + 32 * i + lr, 2 * ks + h)]);
+      for (int i = 0; i < 2; ++i)
+        av[i] = A_IC ? km_frag(reinterpret_cast<const uint16_t*>(sA[buf]), 64 * wm + 32 * i, ks,
+                               lane)
+                     : as_bf16x8(sA[buf][sw64(64 * wm + 32 * i + lr, 2 * ks + h)]);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) bv[f] = as_bf16x8(sB[buf][sw64(64 * wn + 32 * f + lr, 2 * ks + h)]);
+      for (int f = 0; f < 2; ++f)
+        bv[f] = B_IC ? km_frag(reinterpret_cast<const uint16_t*>(sB[buf]), 64 * wn + 32 * f, ks,
+                               lane)
+                     : as_bf16x8(sB[buf][sw64(64 * wn + 32 * f + lr, 2 * ks + h)]);
+      // transposed tile: rows n (B), columns m (A)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int f = 0; f < 2; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[f], acc[i][f], 0, 0, 0);
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[f], av[i], acc[i][f], 0, 0, 0);
     }
     if (s + 1 < nst) {
       store(buf ^ 1);
@@ -192,24 +213,32 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmArgs g) {
     }
   }
 
-  // Epilogue: rows are slot rows (m_is_slots) or rows of the expert's
-  // output matrix.
+  // Epilogue: lane holds output row m = lane % 32 of its fragment and, for
+  // q = 0..3, columns 8 q + 4 (lane / 32) + [0, 4). Rows are slot rows
+  // (m_is_slots) or rows of the expert's output matrix.
   char* cbase = static_cast<char*>(g.c);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + 64 * wm + 32 * i + lr;
+    if (m >= M) continue;
+    const long long row = g.m_is_slots ? (long long)g.offsets[e] + m : (long long)e * g.M + m;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        const int n = n0 + 64 * wn + 32 * f + lr;
-        if (m >= M || n >= N) continue;
-        const long long row = g.m_is_slots ? (long long)g.offsets[e] + m
-                                           : (long long)e * g.M + m;
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 64 * wn + 32 * f + 8 * q + 4 * h;
+        if (n >= N) continue;
         const long long idx = row * g.c_ld + n;
-        if (OUT_F32) reinterpret_cast<float*>(cbase)[idx] = acc[i][f][v];
-        else reinterpret_cast<uint16_t*>(cbase)[idx] = f32_to_bf16(acc[i][f][v]);
+        const f32x16_t& a = acc[i][f];
+        if (OUT_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(cbase) + idx) =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        } else {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(cbase) + idx) =
+              make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+        }
       }
+  }
 }
 
 void launch_bwd_gemm(const BwdGemmArgs& g, bool a_ic, bool b_ic, bool out_f32, int grid,

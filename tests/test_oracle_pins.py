@@ -591,14 +591,15 @@ def test_a8_zero_routing_is_exact_identity():
 # ----------------------------------------------------------------------------
 
 
-def _torch_layer_grads(x, w_router, bias, k, n_ffn, experts, dy):
+def _torch_layer_grads(x, w_router, bias, k, n_ffn, experts, dy, idx=None):
     """The layer in torch with autograd on x, W_r and the expert weights; the
-    selection (piecewise constant) is taken from the oracle's routing."""
+    selection (piecewise constant) is the given one, else the oracle's."""
     X = torch.tensor(x, dtype=torch.float64, requires_grad=True)
     Wr = torch.tensor(np.asarray(w_router, np.float64), requires_grad=True)
     W13 = {e: torch.tensor(np.asarray(a, np.float64), requires_grad=True) for e, (a, _) in experts.items()}
     W2 = {e: torch.tensor(np.asarray(b, np.float64), requires_grad=True) for e, (_, b) in experts.items()}
-    idx = oracle.route(x, w_router, bias, k)["idx"]
+    if idx is None:
+        idx = oracle.route(x, w_router, bias, k)["idx"]
     p = torch.softmax(X @ Wr.T, dim=1)
     y = torch.zeros_like(X)
     for t in range(x.shape[0]):
@@ -612,8 +613,11 @@ def _torch_layer_grads(x, w_router, bias, k, n_ffn, experts, dy):
                 v = X[t]
             y[t] = y[t] + p[t, e] * v
     (y * torch.tensor(dy)).sum().backward()
-    return X.grad.numpy(), Wr.grad.numpy(), {e: W13[e].grad.numpy() for e in W13}, \
-        {e: W2[e].grad.numpy() for e in W2}
+    def grad(w):
+        return np.zeros(tuple(w.shape)) if w.grad is None else w.grad.numpy()
+
+    return X.grad.numpy(), Wr.grad.numpy(), {e: grad(W13[e]) for e in W13}, \
+        {e: grad(W2[e]) for e in W2}
 
 
 @pytest.mark.parametrize("T,seed", [(16, 0), (40, 7)])
@@ -635,6 +639,35 @@ def test_layer_backward_matches_torch_autograd(T, seed):
             assert np.allclose(got["dw2"][e], dw2[e], rtol=1e-10, atol=1e-12)
         else:  # untouched expert: zero gradient
             assert not dw13[e].any() and not dw2[e].any()
+
+
+def test_layer_backward_given_selection():
+    # an imposed selection (another valid one: K distinct experts per token)
+    # gives the autograd gradients of the layer routed that way
+    cfg = inputs.CONFIGS["tiny"]
+    L = inputs.make_layer(cfg, "cpu")
+    T = 12
+    x = bf16_values(inputs.make_tokens(cfg, "cpu", tokens=T))
+    wr, b = L["w_router"].numpy(), L["bias"].numpy()
+    get = expert_getter(L, cfg)
+    experts = {e: get(e) for e in range(cfg.n_ffn)}
+    dy = np.random.default_rng(11).normal(size=x.shape)
+    rng = np.random.default_rng(12)
+    idx = np.stack([rng.permutation(cfg.n_experts)[: cfg.k] for _ in range(T)])
+    assert not np.array_equal(idx, oracle.route(x, wr, b, cfg.k)["idx"])
+    got = oracle.layer_backward(x, wr, b, cfg.k, cfg.n_ffn, get, dy, idx=idx)
+    dx, dwr, dw13, dw2 = _torch_layer_grads(x, wr, b, cfg.k, cfg.n_ffn, experts, dy, idx=idx)
+    assert np.array_equal(got["routing"]["idx"], idx)
+    assert np.allclose(got["dx"], dx, rtol=1e-10, atol=1e-12)
+    assert np.allclose(got["dw_router"], dwr, rtol=1e-10, atol=1e-12)
+    for e in got["dw13"]:
+        assert np.allclose(got["dw13"][e], dw13[e], rtol=1e-10, atol=1e-12)
+        assert np.allclose(got["dw2"][e], dw2[e], rtol=1e-10, atol=1e-12)
+    # its own selection passed explicitly changes nothing
+    own = oracle.route(x, wr, b, cfg.k)["idx"]
+    a = oracle.layer_backward(x, wr, b, cfg.k, cfg.n_ffn, get, dy)
+    c = oracle.layer_backward(x, wr, b, cfg.k, cfg.n_ffn, get, dy, idx=own)
+    assert np.array_equal(a["dx"], c["dx"]) and np.array_equal(a["dw_router"], c["dw_router"])
 
 
 def test_layer_backward_finite_differences():
