@@ -230,8 +230,9 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
  *   dw13       [N][2I][d] bf16 device, written (zero for untouched experts)
  *   dw2        [N][d][I] bf16 device, written (zero for untouched experts)
  *   ws         >= lcmoe_backward_workspace_bytes(shape, T) bytes
- * Errors as lcmoe_forward; UNSUPPORTED for fp8 weights. T = 0 zeroes the
- * weight gradients. */
+ * Errors as lcmoe_forward; UNSUPPORTED for fp8 weights and for
+ * T * max(d, 2I) * 2 >= 2^32 (the grouped GEMMs address an expert's slot
+ * rows with 32-bit byte offsets). T = 0 zeroes the weight gradients. */
 size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens);
 lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                             const float* w_router, const float* bias, const void* w13,
@@ -239,8 +240,9 @@ lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_b
                             void* dw13, void* dw2, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 /* The same call, recording the caller's 10 events (array, may be NULL) at
- * stage boundaries: start, routing, u, W2^T dy, per-row/router, dx rows,
- * dW2, dW13, router gradients, dx. */
+ * stage boundaries: start, routing (with the gather of each FFN slot's x
+ * and dy rows into slot order), u, W2^T dy, per-row/router, dx rows, dW2,
+ * dW13, router gradients, dx. */
 lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                                    const float* w_router, const float* bias, const void* w13,
                                    const void* w2, const void* dy_bf16, float* dx,

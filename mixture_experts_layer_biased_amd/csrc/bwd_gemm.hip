@@ -1,30 +1,40 @@
 // Grouped GEMMs of the backward pass (bf16 operands, fp32 accumulation on
-// v_mfma_f32_32x32x16_bf16), one kernel for the four operand arrangements
-// the backward needs:
+// v_mfma_f32_32x32x16_bf16):
 //
 //   C_e[m][n] = sum_k A_e(m, k) * B_e(n, k)   for every FFN expert e
 //
-// Each operand is a bf16 matrix view: element (i, k) lives at
-//   row(i) * ld + k   ("k-contiguous", rows indexed by i), or
-//   row(k) * ld + i   ("i-contiguous", rows indexed by k),
-// where a row index is one of: a row of the expert's weight matrix (base +
-// e * estride), a slot row of the expert's FFN slots (offsets[e] + r), or
-// the token of such a slot (perm[offsets[e] + r] / K). The expert's extent
-// is either M = its slot count (dgrad: one output row per slot) or K = its
-// slot count (wgrad: the reduction runs over the expert's slots).
+// Two modes:
+//   dgrad: M = the expert's slot count. A is a matrix of slot rows stored
+//     k-contiguous (the gathered x or dy rows, or dU); B is the expert's
+//     weight matrix, k-contiguous (W13 for U = X W13^T) or i-contiguous (W2
+//     for W2^T dy, W13 for dU W13). Output rows are slot rows.
+//   wgrad: K = the expert's slot count. A and B are slot-row matrices read
+//     i-contiguous (element (i, k) at row k, column i): dW2 = dY^T (g h),
+//     dW13 = dU^T X. Output rows are rows of the expert's gradient matrix;
+//     an expert without slots gets zeros.
 //
-// Tiles of 128 x 128 x 32, 256 threads (2 x 2 waves of 64 x 64 = 2 x 2
-// fragments), register-staged double buffering: the next k stage is loaded
-// into registers while the current one is multiplied from LDS. Both
-// operand forms are stored in LDS as they sit in memory, 16 bytes at a time:
-//   k-contiguous: [128 rows][32 k] (64-byte rows, chunk c of row r at
-//     c ^ ((r >> 2) & 3)), read with 16-byte loads;
-//   i-contiguous: [32 k][128 i] (256-byte rows, 64-byte window w of row k at
-//     w ^ (k & 3)), read with the gfx950 transposing LDS load
-//     (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one i.
-// The MFMA computes the transposed tile (B as its first operand), so each
-// lane holds 4 consecutive n of one output row: 16-byte (fp32) or 8-byte
+// Tiles of BM x BN (64 x 64 per wave, 2 x 2 fragments of 32 x 32), k stages
+// of 64 moved HBM/L2 -> LDS by global_load_lds_dwordx4 (one instruction fills
+// 1 KB of LDS) in a ring of NSLOT stages, as in the forward's large-M kernel:
+// per stage, wait for this wave's copies of the stage, a raw barrier, queue
+// the stage NSLOT-1 ahead into the slot just freed, multiply.
+//
+// LDS tile forms, both conflict-free for 16-lane groups:
+//   k-contiguous [rows][64 k]: 128-byte rows, chunk c of row r at
+//     c ^ ((r >> 1) & 7); MFMA operands read with 16-byte loads.
+//   i-contiguous [64 k][128 i] sub-tiles: 256-byte rows, 64-byte window w of
+//     row k at w ^ (k & 3); operands read with ds_read_b64_tr_b16, the gfx950
+//     transposing LDS load, which gives each lane 4 consecutive k of one i.
+// The MFMA computes the transposed tile (B as its first operand), so a lane
+// holds 4 consecutive output columns of one row: 16-byte (fp32) or 8-byte
 // (bf16) stores.
+//
+// Work items are laid out per XCD (blockIdx % 8): each XCD takes a
+// contiguous run of (expert, n tile, m tile) (dgrad) or (expert, m tile,
+// n tile) (wgrad), so the M tiles of one weight tile, and all tiles of one
+// expert's operands, meet in one L2.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,140 +42,226 @@ namespace lcmoe {
 
 namespace {
 
-constexpr int BT = 128;  // tile rows (m and n)
-constexpr int BKB = 32;  // k per stage
+constexpr int BK = 64;  // k per stage
 
-__device__ __forceinline__ int sw64(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+template <int N>
+__device__ __forceinline__ void bwait_vmcnt() {
+  // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Wait until at most n (0..31) of this wave's vector memory operations remain.
+__device__ __forceinline__ void bwait_vmcnt_upto(int n) {
+  switch (n) {
+    case 0: bwait_vmcnt<0>(); break;
+    case 1: bwait_vmcnt<1>(); break;
+    case 2: bwait_vmcnt<2>(); break;
+    case 3: bwait_vmcnt<3>(); break;
+    case 4: bwait_vmcnt<4>(); break;
+    case 5: bwait_vmcnt<5>(); break;
+    case 6: bwait_vmcnt<6>(); break;
+    case 7: bwait_vmcnt<7>(); break;
+    case 8: bwait_vmcnt<8>(); break;
+    case 9: bwait_vmcnt<9>(); break;
+    case 10: bwait_vmcnt<10>(); break;
+    case 11: bwait_vmcnt<11>(); break;
+    case 12: bwait_vmcnt<12>(); break;
+    case 13: bwait_vmcnt<13>(); break;
+    case 14: bwait_vmcnt<14>(); break;
+    case 15: bwait_vmcnt<15>(); break;
+    case 16: bwait_vmcnt<16>(); break;
+    case 17: bwait_vmcnt<17>(); break;
+    case 18: bwait_vmcnt<18>(); break;
+    case 19: bwait_vmcnt<19>(); break;
+    case 20: bwait_vmcnt<20>(); break;
+    case 21: bwait_vmcnt<21>(); break;
+    case 22: bwait_vmcnt<22>(); break;
+    case 23: bwait_vmcnt<23>(); break;
+    default: bwait_vmcnt<24>(); break;
+  }
+}
+__device__ __forceinline__ void braw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// global_load_lds_dwordx4, scalar-base form: lane l copies 16 bytes from
+// sbase + voff into LDS at lds + 16 l. Inline asm, so the compiler does not
+// track it; every wait on these copies is an explicit vmcnt wait.
+__device__ __forceinline__ void bdma16(const char* sbase, uint32_t voff, const uint4* lds) {
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(bs), "s"(l) : "memory");
+}
 
-// i-contiguous tile [32 k][128 i]: element offset of (k, i), i a multiple of 4.
-__device__ __forceinline__ int swkm(int k, int i) {
+// k-contiguous tile: chunk offset of (row, chunk), 128-byte rows.
+__device__ __forceinline__ int kc_off(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+// i-contiguous [64 k][128 i] sub-tile: element offset of (k, i), i % 4 == 0.
+__device__ __forceinline__ int km_off(int k, int i) {
   return k * 128 + ((((i >> 5) ^ (k & 3)) << 5) | (i & 31));
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// MFMA operand (rows base + lane % 32, k 16 ks + 8 (lane / 32) + [0, 8)) from
-// an i-contiguous tile. ds_read_b64_tr_b16 works on groups of 16 lanes: lane
-// s of a group names 4 consecutive i of one k row; the lane j of the group
-// receives, for t = 0..3, element j % 4 of the group's lane j / 4 + 4 t. With
-// lane s reading row k0 + s / 4 at i0 + 4 (s % 4), lane j gets (i0 + j,
-// k0 + t): four consecutive k of one row of the operand.
-__device__ __forceinline__ bf16x8_t km_frag(const uint16_t* tile, int base, int ks, int lane) {
+// MFMA operand (rows base + lane % 32, k 16 kk + 8 (lane / 32) + [0, 8)) from
+// an i-contiguous sub-tile. ds_read_b64_tr_b16 works on groups of 16 lanes:
+// lane s of a group names 4 consecutive i of one k row, and lane j of the
+// group receives, for t = 0..3, element j % 4 of the group's lane j / 4 + 4 t.
+// With lane s reading row k0 + s / 4 at i0 + 4 (s % 4), lane j gets
+// (i0 + j, k0 + t): four consecutive k of one operand row.
+__device__ __forceinline__ bf16x8_t km_frag(const uint4* sub, int base, int kk, int lane) {
+  const uint16_t* tile = reinterpret_cast<const uint16_t*>(sub);
   const int g = lane >> 4, s = lane & 15;
   const int i = base + 16 * (g & 1) + 4 * (s & 3);
-  const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
-  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(tile + swkm(k, i)));
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(tile + swkm(k + 4, i)));
+  const int k = 16 * kk + 8 * (g >> 1) + (s >> 2);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + km_off(k, i)));
+  const s16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + km_off(k + 4, i)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-struct OpView {
-  const uint16_t* base;
-  long long ld;
-  long long estride;  // weight rows: element offset per expert
-  int ic;             // 1: i-contiguous
-  int rows;           // BwdRow: 0 weight, 1 slot, 2 token of slot
-};
+// Zero the operand elements whose k (16 kk + 8 h + t within the stage) is at
+// or past krem.
+__device__ __forceinline__ bf16x8_t mask_k(bf16x8_t v, int kk, int h, int krem) {
+  const int k0 = 16 * kk + 8 * h;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if (k0 + t >= krem) v[t] = 0;
+  return v;
+}
 
 }  // namespace
 
-// Row index -> global row of the operand's matrix, for expert e.
-__device__ __forceinline__ long long bwd_row(const BwdGemmArgs& g, int src, int e, int r) {
-  if (src == kBwdRowWeight) return r;
-  const int s = g.offsets[e] + r;
-  return src == kBwdRowSlot ? (long long)s : (long long)(g.perm[s] / g.topk);
-}
+template <bool WGRAD, bool B_KM, bool OUT_F32, int WM, int WN, int NSLOT>
+__global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
+  constexpr bool A_KM = WGRAD;
+  constexpr bool BKM = WGRAD || B_KM;
+  constexpr int NW = WM * WN;
+  constexpr int BM = 64 * WM, BN = 64 * WN;
+  constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per stage
+  constexpr int SLOT = A_CH + B_CH;
+  constexpr int NB = SLOT / 64;                // 1 KB copy blocks per stage
+  constexpr int CPW = NB / NW;                 // copies per wave per stage
+  constexpr int JA = (A_CH / 64) / NW;         // the first JA of them fill A
+  static_assert(NB % NW == 0 && (A_CH / 64) % NW == 0, "copy blocks must split evenly");
+  static_assert(!A_KM || BM % 128 == 0, "i-contiguous tiles are 128 wide");
+  static_assert(!BKM || BN % 128 == 0, "i-contiguous tiles are 128 wide");
+  __shared__ uint4 lds[NSLOT * SLOT];
 
-template <bool A_IC, bool B_IC, bool OUT_F32>
-__global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmArgs g) {
-  __shared__ uint4 sA[2][BT * 4];
-  __shared__ uint4 sB[2][BT * 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int h = lane >> 5, lr = lane & 31;
 
-  // Work item -> (expert, m tile, n tile).
+  // ---- work item -> (expert, m tile, n tile) ----
+  const int ntn = (g.N + BN - 1) / BN;
+  int total;
+  if (WGRAD) total = g.n_ffn * ((g.M + BM - 1) / BM) * ntn;
+  else total = g.tile_prefix[g.n_ffn] * ntn;
+  const int per_xcd = (total + 7) >> 3;
+  const int pos = blockIdx.x >> 3;
+  if (pos >= per_xcd) return;
+  const int L = (int)(blockIdx.x & 7) * per_xcd + pos;
+  if (L >= total) return;
   int e, mt, nt;
-  const int ntn = (g.N + BT - 1) / BT;
-  if (g.m_is_slots) {
-    const int total = g.tile_prefix[g.n_ffn] * ntn;
-    if ((int)blockIdx.x >= total) return;
+  if (WGRAD) {
+    const int mtn = (g.M + BM - 1) / BM;
+    e = L / (mtn * ntn);
+    const int local = L - e * mtn * ntn;
+    mt = local / ntn;
+    nt = local - mt * ntn;
+  } else {
     int lo = 0, hi = g.n_ffn - 1;
-    const int L = blockIdx.x;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (g.tile_prefix[mid] * ntn <= L) lo = mid; else hi = mid - 1;
     }
     e = lo;
+    const int mtiles = g.tile_prefix[e + 1] - g.tile_prefix[e];
     const int local = L - g.tile_prefix[e] * ntn;
-    mt = local / ntn;
-    nt = local - mt * ntn;
-  } else {
-    const int ntm = (g.M + BT - 1) / BT;
-    const int per = ntm * ntn;
-    e = blockIdx.x / per;
-    if (e >= g.n_ffn) return;
-    const int local = blockIdx.x - e * per;
-    mt = local / ntn;
-    nt = local - mt * ntn;
+    nt = local / mtiles;
+    mt = local - nt * mtiles;
   }
   const int cnt = g.counts[e];
-  const int M = g.m_is_slots ? cnt : g.M;
+  const int off_e = g.offsets[e];
+  const int M = WGRAD ? g.M : cnt;
   const int N = g.N;
-  const int K = g.m_is_slots ? g.K : cnt;
-  const int m0 = mt * BT, n0 = nt * BT;
+  const int K = WGRAD ? cnt : g.K;
+  const int m0 = mt * BM, n0 = nt * BN;
 
-  const uint16_t* abase = g.a + (g.a_rows == kBwdRowWeight ? (long long)e * g.a_estride : 0);
-  const uint16_t* bbase = g.b + (g.b_rows == kBwdRowWeight ? (long long)e * g.b_estride : 0);
+  // Operand bases (bytes): A slot rows start at the expert's first slot; B
+  // is the expert's weight matrix (dgrad) or its slot rows (wgrad).
+  const char* abase = reinterpret_cast<const char*>(g.a) + (size_t)off_e * g.a_ld * 2;
+  const char* bbase = reinterpret_cast<const char*>(g.b) +
+                      (WGRAD ? (size_t)off_e * g.b_ld * 2 : (size_t)e * g.b_estride * 2);
+  const int nst = (K + BK - 1) / BK;
+  const bool half_tail = !WGRAD && (K % BK) != 0;  // dgrad: K is a multiple of 32
 
-  // Staging registers: two 16-byte chunks per operand per thread.
-  uint4 ra[2], rb[2];
-  auto load = [&](int k0) {
+  // ---- per-lane copy descriptors (stage independent) ----
+  // Copy j of this wave fills 1 KB block wave + NW j of the stage: A blocks
+  // first, then B. k-contiguous block: rows 8 b + lane / 8, chunk lane % 8
+  // of the swizzled row (the lane loads the logical chunk placed there).
+  // i-contiguous block: sub-tile b / 16, k rows 4 (b % 16) + lane / 16.
+  uint32_t voff[CPW];   // byte offset from the stage's scalar base
+  int krow[CPW];        // i-contiguous: k row within the stage
+  bool use[CPW];
+  int kcc = 0;          // k-contiguous: logical chunk of this lane (same for all its blocks)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + 256 * j;
-      // A
-      if (!A_IC) {
-        const int r = q >> 2, c = q & 3;
-        const int i = m0 + r, k = k0 + 8 * c;
-        ra[j] = make_uint4(0, 0, 0, 0);
-        if (i < M && k < K)
-          ra[j] = *reinterpret_cast<const uint4*>(abase + bwd_row(g, g.a_rows, e, i) * g.a_ld + k);
-      } else {
-        const int kr = q >> 4, ic = q & 15;
-        const int k = k0 + kr, i = m0 + 8 * ic;
-        ra[j] = make_uint4(0, 0, 0, 0);
-        if (k < K && i < M)
-          ra[j] = *reinterpret_cast<const uint4*>(abase + bwd_row(g, g.a_rows, e, k) * g.a_ld + i);
-      }
-      // B
-      if (!B_IC) {
-        const int r = q >> 2, c = q & 3;
-        const int i = n0 + r, k = k0 + 8 * c;
-        rb[j] = make_uint4(0, 0, 0, 0);
-        if (i < N && k < K)
-          rb[j] = *reinterpret_cast<const uint4*>(bbase + bwd_row(g, g.b_rows, e, i) * g.b_ld + k);
-      } else {
-        const int kr = q >> 4, ic = q & 15;
-        const int k = k0 + kr, i = n0 + 8 * ic;
-        rb[j] = make_uint4(0, 0, 0, 0);
-        if (k < K && i < N)
-          rb[j] = *reinterpret_cast<const uint4*>(bbase + bwd_row(g, g.b_rows, e, k) * g.b_ld + i);
-      }
+  for (int j = 0; j < CPW; ++j) {
+    const bool isA = j < JA;
+    const int b = isA ? wave + NW * j : wave + NW * j - A_CH / 64;
+    const bool km = isA ? A_KM : BKM;
+    const long long ld = isA ? g.a_ld : g.b_ld;
+    use[j] = true;
+    krow[j] = 0;
+    if (!km) {
+      const int row = 8 * b + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      kcc = c;
+      // rows: A slot rows m0 + row (< M), B weight rows n0 + row (< N)
+      const int lim = isA ? M - m0 : N - n0;
+      use[j] = 8 * b < lim;
+      const int rr = (isA ? m0 : n0) + (row < lim ? row : (lim > 0 ? lim - 1 : 0));
+      voff[j] = (uint32_t)((size_t)rr * ld * 2 + 16 * c);
+    } else {
+      const int q = b >> 4, bb = b & 15;
+      const int k = 4 * bb + (lane >> 4), pc = lane & 15;
+      const int c = ((((pc >> 2) ^ (k & 3))) << 2) | (pc & 3);
+      const int ext = isA ? M : N;
+      int col = (isA ? m0 : n0) + 128 * q + 8 * c;
+      if (col > ext - 8) col = ext - 8;
+      krow[j] = k;
+      voff[j] = (uint32_t)(col * 2);
     }
-  };
-  auto store = [&](int buf) {
+  }
+  int per_stage = 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + 256 * j;
-      if (!A_IC) sA[buf][sw64(q >> 2, q & 3)] = ra[j];
-      else *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(sA[buf]) +
-                                     swkm(q >> 4, 8 * (q & 15))) = ra[j];
-      if (!B_IC) sB[buf][sw64(q >> 2, q & 3)] = rb[j];
-      else *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(sB[buf]) +
-                                     swkm(q >> 4, 8 * (q & 15))) = rb[j];
+  for (int j = 0; j < CPW; ++j) per_stage += (int)use[j];
+
+  auto issue = [&](int s) {
+    const int k0 = s * BK;
+    const int kmax = K - 1 - k0;  // i-contiguous rows past K re-load row K - 1
+    // dgrad tail stage of an odd multiple of 32: k-contiguous chunks 4..7 do
+    // not exist; those lanes load chunk c - 4 (64 bytes back), which no MFMA reads.
+    const uint32_t back = (half_tail && s == nst - 1 && kcc >= 4) ? 64u : 0u;
+    uint4* slot = lds + (s % NSLOT) * SLOT;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      if (!use[j]) continue;
+      const bool isA = j < JA;
+      const int b = wave + NW * j;  // block within the slot (A blocks first)
+      const bool km = isA ? A_KM : BKM;
+      const long long ld = isA ? g.a_ld : g.b_ld;
+      const char* base = isA ? abase : bbase;
+      if (!km) {
+        bdma16(base + 2 * (size_t)k0, voff[j] - back, slot + 64 * b);
+      } else {
+        const int k = krow[j] < kmax ? krow[j] : kmax;
+        bdma16(base + (size_t)k0 * ld * 2, voff[j] + (uint32_t)(k * ld * 2), slot + 64 * b);
+      }
     }
   };
 
@@ -177,51 +273,59 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
 
-  const int h = lane >> 5, lr = lane & 31;
-  const int nst = (K + BKB - 1) / BKB;
-  if (nst > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nst) load((s + 1) * BKB);
+  bwait_vmcnt<0>();  // every load before the copies has landed
+
+  auto compute = [&](int s) {
+    const uint4* A = lds + (s % NSLOT) * SLOT;
+    const uint4* B = A + A_CH;
+    const int krem = K - s * BK;  // valid k in this stage (wgrad tail)
+    const int nkk = WGRAD ? min(4, (krem + 15) >> 4) : ((half_tail && s == nst - 1) ? 2 : 4);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk >= nkk) break;
       bf16x8_t av[2], bv[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = A_IC ? km_frag(reinterpret_cast<const uint16_t*>(sA[buf]), 64 * wm + 32 * i, ks,
-                               lane)
-                     : as_bf16x8(sA[buf][sw64(64 * wm + 32 * i + lr, 2 * ks + h)]);
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * wm + 32 * i;
+        av[i] = A_KM ? km_frag(A + (r >> 7) * 1024, r & 127, kk, lane)
+                     : as_bf16x8(A[kc_off(r + lr, 2 * kk + h)]);
+      }
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        bv[f] = B_IC ? km_frag(reinterpret_cast<const uint16_t*>(sB[buf]), 64 * wn + 32 * f, ks,
-                               lane)
-                     : as_bf16x8(sB[buf][sw64(64 * wn + 32 * f + lr, 2 * ks + h)]);
-      // transposed tile: rows n (B), columns m (A)
+      for (int f = 0; f < 2; ++f) {
+        const int r = 64 * wn + 32 * f;
+        bv[f] = BKM ? km_frag(B + (r >> 7) * 1024, r & 127, kk, lane)
+                    : as_bf16x8(B[kc_off(r + lr, 2 * kk + h)]);
+      }
+      if (WGRAD && 16 * kk + 16 > krem) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) av[i] = mask_k(av[i], kk, h, krem);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) bv[f] = mask_k(bv[f], kk, h, krem);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int f = 0; f < 2; ++f)
           acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[f], av[i], acc[i][f], 0, 0, 0);
     }
-    if (s + 1 < nst) {
-      store(buf ^ 1);
-      __syncthreads();
-    }
+  };
+
+  for (int s = 0; s < NSLOT - 1 && s < nst; ++s) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    bwait_vmcnt_upto(per_stage * min(NSLOT - 2, nst - 1 - s));
+    braw_barrier();
+    if (s + NSLOT - 1 < nst) issue(s + NSLOT - 1);
+    compute(s);
   }
 
-  // Epilogue: lane holds output row m = lane % 32 of its fragment and, for
-  // q = 0..3, columns 8 q + 4 (lane / 32) + [0, 4). Rows are slot rows
-  // (m_is_slots) or rows of the expert's output matrix.
+  // ---- epilogue: lane holds output row m = lane % 32 of its fragment and,
+  // for q = 0..3, columns 8 q + 4 (lane / 32) + [0, 4) ----
   char* cbase = static_cast<char*>(g.c);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + 64 * wm + 32 * i + lr;
     if (m >= M) continue;
-    const long long row = g.m_is_slots ? (long long)g.offsets[e] + m : (long long)e * g.M + m;
+    const long long row = WGRAD ? (long long)e * g.M + m : (long long)off_e + m;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -234,21 +338,66 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmArgs g) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(cbase) + idx) =
               make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         } else {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(cbase) + idx) =
-              make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(cbase) + idx) = make_uint2(
+              pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
         }
       }
   }
 }
 
-void launch_bwd_gemm(const BwdGemmArgs& g, bool a_ic, bool b_ic, bool out_f32, int grid,
-                     hipStream_t s) {
-#define LCMOE_BWD(AI, BI, OF) bwd_gemm_kernel<AI, BI, OF><<<grid, 256, 0, s>>>(g)
-  if (!a_ic && !b_ic) { if (out_f32) LCMOE_BWD(false, false, true); else LCMOE_BWD(false, false, false); }
-  else if (!a_ic && b_ic) { if (out_f32) LCMOE_BWD(false, true, true); else LCMOE_BWD(false, true, false); }
-  else if (a_ic && b_ic) { if (out_f32) LCMOE_BWD(true, true, true); else LCMOE_BWD(true, true, false); }
-  else { if (out_f32) LCMOE_BWD(true, false, true); else LCMOE_BWD(true, false, false); }
-#undef LCMOE_BWD
+// One wave per FFN slot row s < S (S read on the device): the token's x and
+// dy rows copied into slot order.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ dy,
+                                                          const int* __restrict__ perm,
+                                                          const int* __restrict__ s_dev, int topk,
+                                                          int d, uint16_t* __restrict__ xs,
+                                                          uint16_t* __restrict__ dys) {
+  const int lane = threadIdx.x & 63;
+  const int S = *s_dev;
+  const int wpb = blockDim.x >> 6;
+  for (int s = blockIdx.x * wpb + (threadIdx.x >> 6); s < S; s += gridDim.x * wpb) {
+    const size_t t = (size_t)(perm[s] / topk);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
+    const uint4* gr = reinterpret_cast<const uint4*>(dy + t * d);
+    uint4* xo = reinterpret_cast<uint4*>(xs + (size_t)s * d);
+    uint4* go = reinterpret_cast<uint4*>(dys + (size_t)s * d);
+    for (int c = lane; c < (d >> 3); c += 64) {
+      xo[c] = xr[c];
+      go[c] = gr[c];
+    }
+  }
+}
+
+// Grid of the dgrad launch: an upper bound of the work items (every expert's
+// M tiles at 128 rows, over all slots) rounded for the per-XCD layout.
+int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols) {
+  const long long items = (smax / kBwdTileM + n_ffn) * ((n_cols + kBwdTileNDgrad - 1) / kBwdTileNDgrad);
+  return (int)std::min<long long>(items + 8, 1ll << 30);
+}
+int bwd_wgrad_grid(int n_ffn, int M, int N) {
+  const long long items = (long long)n_ffn * ((M + kBwdTileM - 1) / kBwdTileM) *
+                          ((N + kBwdTileNWgrad - 1) / kBwdTileNWgrad);
+  return (int)std::min<long long>(items + 8, 1ll << 30);
+}
+
+void launch_bwd_dgrad(const BwdGemmArgs& g, bool b_km, bool out_f32, int grid, hipStream_t s) {
+  static_assert(kBwdTileM == 128 && kBwdTileNDgrad == 256, "dgrad tile");
+  if (b_km) {
+    if (out_f32) bwd_gemm_kernel<false, true, true, 2, 4, 3><<<grid, 512, 0, s>>>(g);
+    else bwd_gemm_kernel<false, true, false, 2, 4, 3><<<grid, 512, 0, s>>>(g);
+  } else {
+    if (out_f32) bwd_gemm_kernel<false, false, true, 2, 4, 3><<<grid, 512, 0, s>>>(g);
+    else bwd_gemm_kernel<false, false, false, 2, 4, 3><<<grid, 512, 0, s>>>(g);
+  }
+}
+void launch_bwd_wgrad(const BwdGemmArgs& g, int grid, hipStream_t s) {
+  static_assert(kBwdTileM == 128 && kBwdTileNWgrad == 128, "wgrad tile");
+  bwd_gemm_kernel<true, true, false, 2, 2, 2><<<grid, 256, 0, s>>>(g);
+}
+void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,
+                        int topk, int d, uint16_t* xs, uint16_t* dys, int grid, hipStream_t s) {
+  gather_rows_kernel<<<grid, 256, 0, s>>>(x, dy, perm, s_dev, topk, d, xs, dys);
 }
 
 }  // namespace lcmoe

@@ -64,33 +64,33 @@ void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, d
                         float* bias, hipStream_t s);
 
 // Backward grouped GEMMs: C_e[m][n] = sum_k A_e(m, k) B_e(n, k) per FFN
-// expert (see bwd_gemm.hip for the operand views).
-constexpr int kBwdRowWeight = 0;  // row of the expert's weight matrix
-constexpr int kBwdRowSlot = 1;    // slot row offsets[e] + r
-constexpr int kBwdRowToken = 2;   // token of slot row: perm[offsets[e] + r] / K
+// expert (see bwd_gemm.hip). dgrad: A = slot rows (k-contiguous), B = the
+// expert's weight matrix, M = the expert's slot count, output rows = slot
+// rows. wgrad: A and B = slot rows read i-contiguous, K = the slot count,
+// output rows e * M + m.
+constexpr int kBwdTileM = 128;       // rows per M tile (both modes)
+constexpr int kBwdTileNDgrad = 256;  // columns per dgrad tile
+constexpr int kBwdTileNWgrad = 128;  // columns per wgrad tile
 struct BwdGemmArgs {
-  const uint16_t* a;       // A operand base (bf16)
+  const uint16_t* a;       // A base (bf16): slot-row matrix, row 0 = slot row 0
   long long a_ld;          // row stride (elements)
-  long long a_estride;     // per-expert element offset (weight rows)
-  int a_rows;              // kBwdRow* for A's rows
-  const uint16_t* b;
+  const uint16_t* b;       // B base: weights [N][rows][b_ld] (dgrad) or slot rows (wgrad)
   long long b_ld;
-  long long b_estride;
-  int b_rows;
+  long long b_estride;     // dgrad: elements per expert of B
   void* c;                 // output, fp32 or bf16
   long long c_ld;
-  int M, N, K;             // fixed extents (M unused when m_is_slots, K when not)
-  int m_is_slots;          // 1: M = expert's slot count, output rows are slot rows;
-                           // 0: K = slot count, output rows e * M + m
+  int M, N, K;             // fixed extents (M unused in dgrad, K in wgrad)
   const int* counts;
   const int* offsets;
-  const int* perm;
-  const int* tile_prefix;  // [N+1] prefix of ceil(count / 128) (m_is_slots)
-  int topk;
+  const int* tile_prefix;  // [N+1] prefix of ceil(count / kBwdTileM) (dgrad)
   int n_ffn;
 };
-void launch_bwd_gemm(const BwdGemmArgs& g, bool a_ic, bool b_ic, bool out_f32, int grid,
-                     hipStream_t s);
+int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols);
+int bwd_wgrad_grid(int n_ffn, int M, int N);
+void launch_bwd_dgrad(const BwdGemmArgs& g, bool b_km, bool out_f32, int grid, hipStream_t s);
+void launch_bwd_wgrad(const BwdGemmArgs& g, int grid, hipStream_t s);
+void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,
+                        int topk, int d, uint16_t* xs, uint16_t* dys, int grid, hipStream_t s);
 void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, hipStream_t s);
 void launch_bwd_rows(const float* U, const float* Q, const int* perm, const float* gate,
                      const int* s_dev, int I, uint16_t* dU, uint16_t* Hg, float* dg, int grid,

@@ -99,8 +99,8 @@ Layout make_layout(const lcmoe_shape& s, int T) {
 // layout, then the backward's own buffers (S = T * min(K, N) slot rows).
 struct BwdLayout {
   Layout f;
-  size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, U = 0, Q = 0, dU = 0, Hg = 0,
-         dXs = 0, dg = 0, dz = 0, dxr = 0, total = 0;
+  size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, Xs = 0, dYs = 0, U = 0, Q = 0,
+         dU = 0, Hg = 0, dXs = 0, dg = 0, dz = 0, dxr = 0, total = 0;
 };
 
 BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
@@ -119,6 +119,8 @@ BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
   B.counts = take((size_t)E * 4);
   B.logits = take((size_t)T * E * 4);
   B.tprefix = take((size_t)(N + 1) * 4);
+  B.Xs = take((size_t)S * d * 2);
+  B.dYs = take((size_t)S * d * 2);
   B.U = take((size_t)S * 2 * I * 4);
   B.Q = take((size_t)S * I * 4);
   B.dU = take((size_t)S * 2 * I * 2);
@@ -411,6 +413,9 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
   const int N = shape->n_ffn, d = shape->d_model, I = shape->d_expert, K = shape->top_k;
   const int E = (int)n_experts(*shape);
+  // the grouped GEMMs address one expert's slot rows (up to T of them) with
+  // 32-bit byte offsets
+  if ((long long)T * std::max(d, 2 * I) * 2 >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
   if (T == 0) {  // no tokens: every gradient is zero
     if (hipMemsetAsync(dw_router, 0, (size_t)E * d * 4, stream) != hipSuccess ||
         hipMemsetAsync(dw13, 0, (size_t)N * 2 * I * d * 2, stream) != hipSuccess ||
@@ -438,6 +443,8 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   int* perm = at<int>(base, L.perm);
   int* row_of_slot = at<int>(base, L.row_of_slot);
   int* tprefix = at<int>(base, B.tprefix);
+  uint16_t* Xs = at<uint16_t>(base, B.Xs);
+  uint16_t* dYs = at<uint16_t>(base, B.dYs);
   float* U = at<float>(base, B.U);
   float* Q = at<float>(base, B.Q);
   uint16_t* dU = at<uint16_t>(base, B.dU);
@@ -446,9 +453,11 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   float* dg = at<float>(base, B.dg);
   float* dz = at<float>(base, B.dz);
   float* dxr = at<float>(base, B.dxr);
+  const int* s_dev = at<int>(base, L.meta) + 2;  // FFN slot count
 
   // 1. routing as in the forward (same kernels, so the same selection), with
-  //    the fp32 logits kept for the softmax backward, and the permutation
+  //    the fp32 logits kept for the softmax backward; the permutation; the
+  //    x and dy rows of every FFN slot gathered into slot order
   mark(ev, 0, stream);
   launch_router(x, w_router, at<float>(base, L.zpart), T, E, d, L.ks, L.kchunk, stream);
   launch_topk(at<float>(base, L.zpart), L.ks, bias, T, E, K, idx, gate, logits, stream);
@@ -456,64 +465,57 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
                  at<int>(base, L.tilecnt), at<int>(base, L.tileoff), counts, offsets,
                  at<int>(base, L.small_list), at<int>(base, L.mt_prefix), at<int>(base, L.meta),
                  perm, row_of_slot, stream);
-  launch_tile_prefix(counts, N, 128, tprefix, stream);
+  launch_tile_prefix(counts, N, kBwdTileM, tprefix, stream);
+  const long long smax = L.smax;
+  const int row_grid = (int)std::min<long long>(4096, (smax + 3) / 4);
+  launch_gather_rows(x, dy, perm, s_dev, K, d, Xs, dYs, row_grid, stream);
   mark(ev, 1, stream);
 
-  const long long smax = L.smax;
-  auto slot_grid = [&](int n) {  // upper bound of (m tiles over all experts) x (n tiles)
-    return (int)std::min<long long>((smax / 128 + N) * ((n + 127) / 128), 1ll << 30);
-  };
   BwdGemmArgs g{};
   g.counts = counts;
   g.offsets = offsets;
-  g.perm = perm;
   g.tile_prefix = tprefix;
-  g.topk = K;
   g.n_ffn = N;
 
   // 2. U = X_e W13_e^T (pre-activations, fp32), per FFN slot row
-  g.a = x; g.a_ld = d; g.a_estride = 0; g.a_rows = kBwdRowToken;
+  g.a = Xs; g.a_ld = d;
   g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
-  g.b_rows = kBwdRowWeight;
-  g.c = U; g.c_ld = 2 * I; g.N = 2 * I; g.K = d; g.m_is_slots = 1;
-  launch_bwd_gemm(g, false, false, true, slot_grid(2 * I), stream);
+  g.c = U; g.c_ld = 2 * I; g.N = 2 * I; g.K = d;
+  launch_bwd_dgrad(g, false, true, bwd_dgrad_grid(smax, N, 2 * I), stream);
   mark(ev, 2, stream);
 
   // 3. Q = dY_e W2_e (W2 read k-major), per FFN slot row
-  g.a = dy; g.a_ld = d; g.a_rows = kBwdRowToken;
+  g.a = dYs; g.a_ld = d;
   g.b = static_cast<const uint16_t*>(w2); g.b_ld = I; g.b_estride = (long long)d * I;
-  g.b_rows = kBwdRowWeight;
-  g.c = Q; g.c_ld = I; g.N = I; g.K = d; g.m_is_slots = 1;
-  launch_bwd_gemm(g, false, true, true, slot_grid(I), stream);
+  g.c = Q; g.c_ld = I; g.N = I; g.K = d;
+  launch_bwd_dgrad(g, true, true, bwd_dgrad_grid(smax, N, I), stream);
   mark(ev, 3, stream);
 
   // 4. per slot row: dg, dU, g*h; zero-slot dg; router dz
-  launch_bwd_rows(U, Q, perm, gate, at<int>(base, L.meta) + 2, I, dU, Hg, dg,
-                  (int)std::min<long long>(4096, (smax + 3) / 4), stream);
+  launch_bwd_rows(U, Q, perm, gate, s_dev, I, dU, Hg, dg, row_grid, stream);
   launch_bwd_zero_dg(x, dy, idx, T, d, K, N, dg, stream);
   launch_bwd_router_dz(logits, idx, gate, dg, T, E, K, dz, stream);
   mark(ev, 4, stream);
 
   // 5. dX per slot row = dU_e W13_e (W13 read k-major)
-  g.a = dU; g.a_ld = 2 * I; g.a_rows = kBwdRowSlot;
+  g.a = dU; g.a_ld = 2 * I;
   g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
-  g.b_rows = kBwdRowWeight;
-  g.c = dXs; g.c_ld = d; g.N = d; g.K = 2 * I; g.m_is_slots = 1;
-  launch_bwd_gemm(g, false, true, true, slot_grid(d), stream);
+  g.c = dXs; g.c_ld = d; g.N = d; g.K = 2 * I;
+  launch_bwd_dgrad(g, true, true, bwd_dgrad_grid(smax, N, d), stream);
   mark(ev, 5, stream);
 
   // 6. dW2_e[c][j] = sum over the expert's slots of dy[t][c] (g h)[s][j]
-  g.a = dy; g.a_ld = d; g.a_rows = kBwdRowToken;
-  g.b = Hg; g.b_ld = I; g.b_estride = 0; g.b_rows = kBwdRowSlot;
-  g.c = dw2; g.c_ld = I; g.M = d; g.N = I; g.m_is_slots = 0;
-  launch_bwd_gemm(g, true, true, false, N * ((d + 127) / 128) * ((I + 127) / 128), stream);
+  g.a = dYs; g.a_ld = d;
+  g.b = Hg; g.b_ld = I; g.b_estride = 0;
+  g.c = dw2; g.c_ld = I; g.M = d; g.N = I;
+  launch_bwd_wgrad(g, bwd_wgrad_grid(N, d, I), stream);
   mark(ev, 6, stream);
 
   // 7. dW13_e[r][c] = sum over the expert's slots of dU[s][r] x[t][c]
-  g.a = dU; g.a_ld = 2 * I; g.a_rows = kBwdRowSlot;
-  g.b = x; g.b_ld = d; g.b_rows = kBwdRowToken;
-  g.c = dw13; g.c_ld = d; g.M = 2 * I; g.N = d; g.m_is_slots = 0;
-  launch_bwd_gemm(g, true, true, false, N * ((2 * I + 127) / 128) * ((d + 127) / 128), stream);
+  g.a = dU; g.a_ld = 2 * I;
+  g.b = Xs; g.b_ld = d;
+  g.c = dw13; g.c_ld = d; g.M = 2 * I; g.N = d;
+  launch_bwd_wgrad(g, bwd_wgrad_grid(N, 2 * I, d), stream);
   mark(ev, 7, stream);
 
   // 8. router: dW_r = dz^T x, dx_r = dz W_r (fp32)

@@ -194,6 +194,8 @@ def test_backward_validation():
     assert need > 64
     assert _backward(s, 4, ws=FAKE, wsb=64) == ERR_WORKSPACE
     assert _backward(s, 2 ** 31 // 3 + 1) == ERR_UNSUPPORTED   # T*K >= 2^31
+    wide = make_shape(8192, 8, 4, 3, 32)
+    assert _backward(wide, 2 ** 18) == ERR_UNSUPPORTED  # slot rows of 4 GiB (32-bit offsets)
     # fp8 weights: no backward
     for wd in (1, 2):
         f = make_shape(128, 8, 4, 3, 128, wd)
