@@ -103,12 +103,21 @@ __global__ __launch_bounds__(256) void bwd_zero_dg_kernel(const uint16_t* __rest
 }
 
 // One wave per token: p = softmax(z_t) over all E, c = sum_k dg_tk g_tk,
-// dz_i = p_i (dp_i - c) with dp_i = dg_tk at the selected experts.
+// dz_i = p_i (dp_i - c) with dp_i = dg_tk at the selected experts. dz is
+// written as its three exact bf16 planes (hi, mid, lo), experts padded to Ep
+// with zeros, in the two layouts the router-gradient GEMMs read:
+//   dzp[t][6 Ep]: segments (hi, hi, mid, hi, lo, mid), the A operand of
+//     dx_r = dz W_r against W_r's planes (hi, mid, hi, lo, hi, mid): the six
+//     plane products above 2^-24 of the product;
+//   dzt[j T + t][Ep]: plane j, the A operand of dW_r = dz^T x (x is bf16, so
+//     the three plane products are exact).
 __global__ __launch_bounds__(256) void bwd_router_dz_kernel(const float* __restrict__ logits,
                                                             const int* __restrict__ idx,
                                                             const float* __restrict__ gate,
                                                             const float* __restrict__ dg, int T,
-                                                            int E, int K, float* __restrict__ dz) {
+                                                            int E, int Ep, int K,
+                                                            uint16_t* __restrict__ dzp,
+                                                            uint16_t* __restrict__ dzt) {
   const int lane = threadIdx.x & 63;
   const int wpb = blockDim.x >> 6;
   for (int t = blockIdx.x * wpb + (threadIdx.x >> 6); t < T; t += gridDim.x * wpb) {
@@ -121,70 +130,67 @@ __global__ __launch_bounds__(256) void bwd_router_dz_kernel(const float* __restr
     s = wave_sum(s);
     float c = 0.f;
     for (int k = 0; k < K; ++k) c += dg[(size_t)t * K + k] * gate[(size_t)t * K + k];
-    for (int i = lane; i < E; i += 64) {
-      float dp = 0.f;
-      for (int k = 0; k < K; ++k)
-        if (idx[(size_t)t * K + k] == i) dp = dg[(size_t)t * K + k];
-      const float p = expf(z[i] - m) / s;
-      dz[(size_t)t * E + i] = p * (dp - c);
+    uint16_t* prow = dzp + (size_t)t * 6 * Ep;
+    for (int i = lane; i < Ep; i += 64) {
+      float v = 0.f;
+      if (i < E) {
+        float dp = 0.f;
+        for (int k = 0; k < K; ++k)
+          if (idx[(size_t)t * K + k] == i) dp = dg[(size_t)t * K + k];
+        const float p = expf(z[i] - m) / s;
+        v = p * (dp - c);
+      }
+      uint16_t hi, mid, lo;
+      split3(v, hi, mid, lo);
+      prow[i] = hi;
+      prow[Ep + i] = hi;
+      prow[2 * Ep + i] = mid;
+      prow[3 * Ep + i] = hi;
+      prow[4 * Ep + i] = lo;
+      prow[5 * Ep + i] = mid;
+      dzt[(size_t)t * Ep + i] = hi;
+      dzt[((size_t)T + t) * Ep + i] = mid;
+      dzt[((size_t)2 * T + t) * Ep + i] = lo;
     }
   }
 }
 
-// fp32 GEMM for the router gradients, C[m][n] = sum_k A(m, k) B(n, k):
-// A(m, k) at a[m * lda + k] (A_T: a[k * lda + m]); B(n, k) likewise, B in
-// fp32 or bf16. 64 x 64 tiles, k stages of 16, 256 threads with 4 x 4
-// outputs each, fp32 FMA in k order. Grid: x over m tiles, y over n tiles.
-template <bool A_T, bool B_T, bool B_BF16>
-__global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__ a, long long lda,
-                                                       const void* __restrict__ bv, long long ldb,
-                                                       float* __restrict__ c, long long ldc,
-                                                       int M, int N, int K) {
-  __shared__ float sa[16][64 + 1];
-  __shared__ float sb[16][64 + 1];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-  const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int q = tid; q < 16 * 64; q += 256) {
-      const int kk = A_T ? q >> 6 : q & 15, mm = A_T ? q & 63 : q >> 4;
-      const int gm = m0 + mm, gk = k0 + kk;
-      sa[kk][mm] = (gm < M && gk < K)
-                       ? (A_T ? a[(long long)gk * lda + gm] : a[(long long)gm * lda + gk])
-                       : 0.f;
-      const int kb = B_T ? q >> 6 : q & 15, nn = B_T ? q & 63 : q >> 4;
-      const int gn = n0 + nn, gk2 = k0 + kb;
-      float bvv = 0.f;
-      if (gn < N && gk2 < K) {
-        const long long off = B_T ? (long long)gk2 * ldb + gn : (long long)gn * ldb + gk2;
-        bvv = B_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(bv)[off])
-                     : static_cast<const float*>(bv)[off];
-      }
-      sb[kb][nn] = bvv;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = sa[kk][tm + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bw[j] = sb[kk][tn + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bw[j], acc[i][j]);
-    }
-    __syncthreads();
+// W_r's planes stacked to match dzp: wsp[s Ep + i][c] for segments s = 0..5
+// = planes (hi, mid, hi, lo, hi, mid) of W_r[i][c], rows i >= E zero. Thread
+// 0 also writes the one-group metadata of the two router-gradient GEMMs:
+// rg = {T, 0, 0, ceil(T / 128), 3 T, 0} (counts, offsets and tile prefix of
+// dx_r; counts and offsets of dW_r).
+__global__ __launch_bounds__(256) void router_w_split_kernel(const float* __restrict__ wr, int E,
+                                                             int Ep, int d, int T,
+                                                             uint16_t* __restrict__ wsp,
+                                                             int* __restrict__ rg) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    rg[0] = T;
+    rg[1] = 0;
+    rg[2] = 0;
+    rg[3] = (T + kBwdTileM - 1) / kBwdTileM;
+    rg[4] = 3 * T;
+    rg[5] = 0;
   }
+  const long long n4 = (long long)Ep * d / 4;
+  for (long long q = blockIdx.x * 256ll + threadIdx.x; q < n4; q += (long long)gridDim.x * 256) {
+    const long long el = q * 4;
+    const int i = (int)(el / d), c = (int)(el - (long long)i * d);
+    float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < E) w = *reinterpret_cast<const float4*>(wr + (size_t)i * d + c);
+    uint16_t h[4], m[4], l[4];
+    split3(w.x, h[0], m[0], l[0]);
+    split3(w.y, h[1], m[1], l[1]);
+    split3(w.z, h[2], m[2], l[2]);
+    split3(w.w, h[3], m[3], l[3]);
+    const uint2 H = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+    const uint2 M = make_uint2(m[0] | (uint32_t)m[1] << 16, m[2] | (uint32_t)m[3] << 16);
+    const uint2 Lo = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
+    const uint2 seg[6] = {H, M, H, Lo, H, M};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gm = m0 + tm + i, gn = n0 + tn + j;
-      if (gm < M && gn < N) c[(long long)gm * ldc + gn] = acc[i][j];
-    }
+    for (int sg = 0; sg < 6; ++sg)
+      *reinterpret_cast<uint2*>(wsp + ((size_t)sg * Ep + i) * d + c) = seg[sg];
+  }
 }
 
 // One block per token: dx_t = sum over its FFN slots (k order) of the dXs
@@ -230,18 +236,37 @@ void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, i
   bwd_zero_dg_kernel<<<grid, 256, 0, s>>>(x, dy, idx, T, d, K, N, dg);
 }
 void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate, const float* dg,
-                          int T, int E, int K, float* dz, hipStream_t s) {
+                          int T, int E, int Ep, int K, uint16_t* dzp, uint16_t* dzt, hipStream_t s) {
   const int grid = std::max(1, std::min(2048, (T + 3) / 4));
-  bwd_router_dz_kernel<<<grid, 256, 0, s>>>(logits, idx, gate, dg, T, E, K, dz);
+  bwd_router_dz_kernel<<<grid, 256, 0, s>>>(logits, idx, gate, dg, T, E, Ep, K, dzp, dzt);
 }
-void launch_router_grads(const float* dz, const uint16_t* x, const float* wr, int T, int E, int d,
-                         float* dwr, float* dxr, hipStream_t s) {
-  // dW_r[i][c] = sum_t dz[t][i] x[t][c]
-  f32_gemm_kernel<true, true, true><<<dim3((E + 63) / 64, (d + 63) / 64), 256, 0, s>>>(
-      dz, E, x, d, dwr, d, E, d, T);
-  // dxr[t][c] = sum_i dz[t][i] W_r[i][c]
-  f32_gemm_kernel<false, true, false><<<dim3((T + 63) / 64, (d + 63) / 64), 256, 0, s>>>(
-      dz, E, wr, d, dxr, d, T, d, E);
+bool launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_t* x,
+                         const float* wr, int T, int E, int Ep, int d, uint16_t* wsp,
+                         uint16_t* x3, int* rg, float* dwr, float* dxr, hipStream_t s) {
+  const long long n4 = (long long)Ep * d / 4;
+  router_w_split_kernel<<<(int)std::min<long long>(4096, (n4 + 255) / 256), 256, 0, s>>>(
+      wr, E, Ep, d, T, wsp, rg);
+  for (int j = 0; j < 3; ++j)
+    if (hipMemcpyAsync(x3 + (size_t)j * T * d, x, (size_t)T * d * 2, hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return false;
+  BwdGemmArgs g{};
+  g.n_ffn = 1;
+  // dx_r[t][c] = sum over the six plane products of dz[t][i] W_r[i][c]
+  g.a = dzp; g.a_ld = 6ll * Ep;
+  g.b = wsp; g.b_ld = d; g.b_estride = 0;
+  g.c = dxr; g.c_ld = d; g.N = d; g.K = 6 * Ep;
+  g.counts = rg; g.offsets = rg + 1; g.tile_prefix = rg + 2;
+  launch_bwd_dgrad(g, true, true, bwd_dgrad_grid(T, 1, d), s);
+  // dW_r[i][c] = sum over the 3 T plane rows of dz[t][i] x[t][c]
+  BwdGemmArgs w{};
+  w.n_ffn = 1;
+  w.a = dzt; w.a_ld = Ep;
+  w.b = x3; w.b_ld = d;
+  w.c = dwr; w.c_ld = d; w.M = Ep; w.m_store = E; w.N = d;
+  w.counts = rg + 4; w.offsets = rg + 5;
+  launch_bwd_wgrad_f32(w, s);
+  return true;
 }
 void launch_bwd_dx(const float* dXs, const uint16_t* dy, const float* dxr, const int* row_of_slot,
                    const float* gate, int T, int d, int K, float* dx, hipStream_t s) {

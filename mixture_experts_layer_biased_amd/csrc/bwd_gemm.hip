@@ -13,8 +13,8 @@
 //     dW13 = dU^T X. Output rows are rows of the expert's gradient matrix;
 //     an expert without slots gets zeros.
 //
-// Tiles of BM x BN (64 x 64 per wave, 2 x 2 fragments of 32 x 32), k stages
-// of 64 moved HBM/L2 -> LDS by global_load_lds_dwordx4 (one instruction fills
+// Tiles of BM x BN (per wave FM x FN fragments of 32 x 32), k stages of 64
+// moved HBM/L2 -> LDS by global_load_lds_dwordx4 (one instruction fills
 // 1 KB of LDS) in a ring of NSLOT stages, as in the forward's large-M kernel:
 // per stage, wait for this wave's copies of the stage, a raw barrier, queue
 // the stage NSLOT-1 ahead into the slot just freed, multiply.
@@ -43,6 +43,13 @@ namespace lcmoe {
 namespace {
 
 constexpr int BK = 64;  // k per stage
+// Weight-gradient tile: 2 x 4 waves of 4 x 2 fragments (256 x 256), two
+// stages of 64 KB in the ring. (Measured at the prefill batch against 128 x
+// 128, 128 x 256 and 256 x 128 tiles and a persistent producer/consumer
+// variant: the largest tile halves the L2 -> LDS bytes per output and wins.)
+constexpr int kWgWM = 2, kWgWN = 4, kWgFM = 4, kWgFN = 2;
+constexpr int kWgradBM = 32 * kWgFM * kWgWM;
+constexpr int kWgradBN = 32 * kWgFN * kWgWN;
 
 template <int N>
 __device__ __forceinline__ void bwait_vmcnt() {
@@ -133,20 +140,67 @@ __device__ __forceinline__ bf16x8_t mask_k(bf16x8_t v, int kk, int h, int krem) 
   return v;
 }
 
+// Store one wave's 64 x 64 output sub-tile (the transposed-MFMA layout: lane
+// holds row 32 i + lane % 32, columns 32 f + 8 q + 4 (lane / 32) + [0, 4))
+// through LDS, so each global store instruction writes whole rows: 128 bytes
+// per row (bf16, 8 rows per instruction) or 256 bytes (fp32, 4 rows).
+// st: this wave's 8 KB (bf16) or 16 KB (fp32) of LDS; rows of 8 or 16
+// chunks, chunk c of row r at c ^ ((r >> 1) & 7) (bf16) or c ^ (r & 15)
+// (fp32), conflict-free for the writes and the row-major reads. obase:
+// element (0, 0) of the sub-tile in the output, ld its row stride; rows at or
+// past rvalid and columns at or past cvalid are not written.
+template <bool F32>
+__device__ __forceinline__ void store_subtile(const f32x16_t (&acc)[2][2], uint4* st, int lane,
+                                              char* obase, long long ld, int rvalid, int cvalid) {
+  constexpr int RC = F32 ? 16 : 8;  // 16-byte chunks per sub-tile row
+  constexpr int ESZ = F32 ? 4 : 2;
+  const int h = lane >> 5, lr = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 32 * i + lr;
+        const f32x16_t& a = acc[i][f];
+        if (F32) {
+          const int c = 8 * f + 2 * q + h;
+          st[r * RC + (c ^ (r & 15))] = make_uint4(__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
+                                                   __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3]));
+        } else {
+          const int c = 4 * f + q;
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(st + r * RC + (c ^ ((r >> 1) & 7))) + 8 * h) =
+              make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+        }
+      }
+  constexpr int RPI = 64 / RC;  // rows per read instruction
+#pragma unroll
+  for (int j = 0; j < 64 / RPI; ++j) {
+    const int r = RPI * j + lane / RC, c = lane % RC;
+    const uint4 v = st[r * RC + (F32 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)))];
+    const int col = c * (16 / ESZ);
+    if (r < rvalid && col < cvalid)
+      *reinterpret_cast<uint4*>(obase + ((long long)r * ld + col) * ESZ) = v;
+  }
+}
+
 }  // namespace
 
-template <bool WGRAD, bool B_KM, bool OUT_F32, int WM, int WN, int NSLOT>
+template <bool WGRAD, bool B_KM, bool OUT_F32, int WM, int WN, int FM, int FN, int NSLOT>
 __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
   constexpr bool A_KM = WGRAD;
   constexpr bool BKM = WGRAD || B_KM;
   constexpr int NW = WM * WN;
-  constexpr int BM = 64 * WM, BN = 64 * WN;
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;  // wave tile (32 FM) x (32 FN)
+  static_assert(FM % 2 == 0 && FN % 2 == 0, "stores go by 64 x 64 sub-tiles");
   constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per stage
   constexpr int SLOT = A_CH + B_CH;
   constexpr int NB = SLOT / 64;                // 1 KB copy blocks per stage
   constexpr int CPW = NB / NW;                 // copies per wave per stage
   constexpr int JA = (A_CH / 64) / NW;         // the first JA of them fill A
   static_assert(NB % NW == 0 && (A_CH / 64) % NW == 0, "copy blocks must split evenly");
+  static_assert(NW * (OUT_F32 ? 1024 : 512) <= NSLOT * SLOT, "epilogue staging fits in the ring");
+  static_assert((NSLOT - 2) * (NB / NW) <= 63, "vmcnt range");
   static_assert(!A_KM || BM % 128 == 0, "i-contiguous tiles are 128 wide");
   static_assert(!BKM || BN % 128 == 0, "i-contiguous tiles are 128 wide");
   __shared__ uint4 lds[NSLOT * SLOT];
@@ -265,11 +319,11 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FN; ++f)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
 
@@ -283,29 +337,29 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk >= nkk) break;
-      bf16x8_t av[2], bv[2];
+      bf16x8_t av[FM], bv[FN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 64 * wm + 32 * i;
+      for (int i = 0; i < FM; ++i) {
+        const int r = 32 * FM * wm + 32 * i;
         av[i] = A_KM ? km_frag(A + (r >> 7) * 1024, r & 127, kk, lane)
                      : as_bf16x8(A[kc_off(r + lr, 2 * kk + h)]);
       }
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int r = 64 * wn + 32 * f;
+      for (int f = 0; f < FN; ++f) {
+        const int r = 32 * FN * wn + 32 * f;
         bv[f] = BKM ? km_frag(B + (r >> 7) * 1024, r & 127, kk, lane)
                     : as_bf16x8(B[kc_off(r + lr, 2 * kk + h)]);
       }
       if (WGRAD && 16 * kk + 16 > krem) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) av[i] = mask_k(av[i], kk, h, krem);
+        for (int i = 0; i < FM; ++i) av[i] = mask_k(av[i], kk, h, krem);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) bv[f] = mask_k(bv[f], kk, h, krem);
+        for (int f = 0; f < FN; ++f) bv[f] = mask_k(bv[f], kk, h, krem);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < FN; ++f)
           acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[f], av[i], acc[i][f], 0, 0, 0);
     }
   };
@@ -318,31 +372,20 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
     compute(s);
   }
 
-  // ---- epilogue: lane holds output row m = lane % 32 of its fragment and,
-  // for q = 0..3, columns 8 q + 4 (lane / 32) + [0, 4) ----
-  char* cbase = static_cast<char*>(g.c);
+  // ---- epilogue through LDS (the ring is free once every wave is done) ----
+  braw_barrier();
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + 64 * wm + 32 * i + lr;
-    if (m >= M) continue;
-    const long long row = WGRAD ? (long long)e * g.M + m : (long long)off_e + m;
+  for (int i2 = 0; i2 < FM / 2; ++i2)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + 64 * wn + 32 * f + 8 * q + 4 * h;
-        if (n >= N) continue;
-        const long long idx = row * g.c_ld + n;
-        const f32x16_t& a = acc[i][f];
-        if (OUT_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(cbase) + idx) =
-              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-        } else {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(cbase) + idx) = make_uint2(
-              pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
-        }
-      }
-  }
+    for (int f2 = 0; f2 < FN / 2; ++f2) {
+      const int r0 = m0 + 32 * FM * wm + 64 * i2, c0 = n0 + 32 * FN * wn + 64 * f2;
+      const long long orow = WGRAD ? (long long)e * g.M + r0 : (long long)off_e + r0;
+      char* obase = static_cast<char*>(g.c) + (orow * g.c_ld + c0) * (OUT_F32 ? 4 : 2);
+      const f32x16_t sub[2][2] = {{acc[2 * i2][2 * f2], acc[2 * i2][2 * f2 + 1]},
+                                  {acc[2 * i2 + 1][2 * f2], acc[2 * i2 + 1][2 * f2 + 1]}};
+      store_subtile<OUT_F32>(sub, lds + wave * (OUT_F32 ? 1024 : 512), lane, obase, g.c_ld,
+                             (WGRAD ? min(M, g.m_store) : M) - r0, N - c0);
+    }
 }
 
 // One wave per FFN slot row s < S (S read on the device): the token's x and
@@ -376,24 +419,29 @@ int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols) {
   return (int)std::min<long long>(items + 8, 1ll << 30);
 }
 int bwd_wgrad_grid(int n_ffn, int M, int N) {
-  const long long items = (long long)n_ffn * ((M + kBwdTileM - 1) / kBwdTileM) *
-                          ((N + kBwdTileNWgrad - 1) / kBwdTileNWgrad);
+  const long long items = (long long)n_ffn * ((M + kWgradBM - 1) / kWgradBM) *
+                          ((N + kWgradBN - 1) / kWgradBN);
   return (int)std::min<long long>(items + 8, 1ll << 30);
 }
 
 void launch_bwd_dgrad(const BwdGemmArgs& g, bool b_km, bool out_f32, int grid, hipStream_t s) {
   static_assert(kBwdTileM == 128 && kBwdTileNDgrad == 256, "dgrad tile");
   if (b_km) {
-    if (out_f32) bwd_gemm_kernel<false, true, true, 2, 4, 3><<<grid, 512, 0, s>>>(g);
-    else bwd_gemm_kernel<false, true, false, 2, 4, 3><<<grid, 512, 0, s>>>(g);
+    if (out_f32) bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
+    else bwd_gemm_kernel<false, true, false, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
   } else {
-    if (out_f32) bwd_gemm_kernel<false, false, true, 2, 4, 3><<<grid, 512, 0, s>>>(g);
-    else bwd_gemm_kernel<false, false, false, 2, 4, 3><<<grid, 512, 0, s>>>(g);
+    if (out_f32) bwd_gemm_kernel<false, false, true, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
+    else bwd_gemm_kernel<false, false, false, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
   }
 }
 void launch_bwd_wgrad(const BwdGemmArgs& g, int grid, hipStream_t s) {
-  static_assert(kBwdTileM == 128 && kBwdTileNWgrad == 128, "wgrad tile");
-  bwd_gemm_kernel<true, true, false, 2, 2, 2><<<grid, 256, 0, s>>>(g);
+  bwd_gemm_kernel<true, true, false, kWgWM, kWgWN, kWgFM, kWgFN, 2>
+      <<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
+}
+void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s) {
+  const long long items = (long long)g.n_ffn * ((g.M + 127) / 128) * ((g.N + 127) / 128);
+  bwd_gemm_kernel<true, true, true, 2, 2, 2, 2, 3>
+      <<<(int)std::min<long long>(items + 8, 1ll << 30), 256, 0, s>>>(g);
 }
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,
                         int topk, int d, uint16_t* xs, uint16_t* dys, int grid, hipStream_t s) {

@@ -59,6 +59,21 @@ __device__ __forceinline__ uint4 fp8x8_scaled_to_bf16x8(uint32_t w0, uint32_t w1
   return r;
 }
 
+// fp32 -> three bf16 planes with w = hi + mid + lo exactly: each residual of
+// a round-to-nearest bf16 conversion is exact in fp32 and the last one fits
+// in 8 bits (Henry, Tang & Heinecke, ARITH 2019). Products of a bf16 value
+// with each plane are exact in an fp32 MFMA accumulator.
+__device__ __forceinline__ void split3(float w, uint16_t& h, uint16_t& m, uint16_t& l) {
+  __bf16 bh = (__bf16)w;
+  float r1 = w - (float)bh;
+  __bf16 bm = (__bf16)r1;
+  float r2 = r1 - (float)bm;
+  __bf16 bl = (__bf16)r2;
+  h = *reinterpret_cast<uint16_t*>(&bh);
+  m = *reinterpret_cast<uint16_t*>(&bm);
+  l = *reinterpret_cast<uint16_t*>(&bl);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return *reinterpret_cast<bf16x8_t*>(&v);
 }

@@ -68,9 +68,8 @@ void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, d
 // expert's weight matrix, M = the expert's slot count, output rows = slot
 // rows. wgrad: A and B = slot rows read i-contiguous, K = the slot count,
 // output rows e * M + m.
-constexpr int kBwdTileM = 128;       // rows per M tile (both modes)
+constexpr int kBwdTileM = 128;       // rows per dgrad M tile (slot rows)
 constexpr int kBwdTileNDgrad = 256;  // columns per dgrad tile
-constexpr int kBwdTileNWgrad = 128;  // columns per wgrad tile
 struct BwdGemmArgs {
   const uint16_t* a;       // A base (bf16): slot-row matrix, row 0 = slot row 0
   long long a_ld;          // row stride (elements)
@@ -80,6 +79,7 @@ struct BwdGemmArgs {
   void* c;                 // output, fp32 or bf16
   long long c_ld;
   int M, N, K;             // fixed extents (M unused in dgrad, K in wgrad)
+  int m_store;             // wgrad: output rows stored, m < min(M, m_store)
   const int* counts;
   const int* offsets;
   const int* tile_prefix;  // [N+1] prefix of ceil(count / kBwdTileM) (dgrad)
@@ -89,6 +89,8 @@ int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols);
 int bwd_wgrad_grid(int n_ffn, int M, int N);
 void launch_bwd_dgrad(const BwdGemmArgs& g, bool b_km, bool out_f32, int grid, hipStream_t s);
 void launch_bwd_wgrad(const BwdGemmArgs& g, int grid, hipStream_t s);
+// wgrad with fp32 output and 128 x 128 tiles (the router gradient: few tiles, long k)
+void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s);
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,
                         int topk, int d, uint16_t* xs, uint16_t* dys, int grid, hipStream_t s);
 void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, hipStream_t s);
@@ -98,9 +100,12 @@ void launch_bwd_rows(const float* U, const float* Q, const int* perm, const floa
 void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, int T, int d, int K,
                         int N, float* dg, hipStream_t s);
 void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate, const float* dg,
-                          int T, int E, int K, float* dz, hipStream_t s);
-void launch_router_grads(const float* dz, const uint16_t* x, const float* wr, int T, int E, int d,
-                         float* dwr, float* dxr, hipStream_t s);
+                          int T, int E, int Ep, int K, uint16_t* dzp, uint16_t* dzt, hipStream_t s);
+// Router gradients on bf16 MFMA from exact planes: dx_r = dz W_r, dW_r = dz^T x.
+// wsp [6 Ep][d], x3 [3 T][d] and rg [6] are scratch. Returns false if a copy fails.
+bool launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_t* x,
+                         const float* wr, int T, int E, int Ep, int d, uint16_t* wsp,
+                         uint16_t* x3, int* rg, float* dwr, float* dxr, hipStream_t s);
 void launch_bwd_dx(const float* dXs, const uint16_t* dy, const float* dxr, const int* row_of_slot,
                    const float* gate, int T, int d, int K, float* dx, hipStream_t s);
 

@@ -100,7 +100,9 @@ Layout make_layout(const lcmoe_shape& s, int T) {
 struct BwdLayout {
   Layout f;
   size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, Xs = 0, dYs = 0, U = 0, Q = 0,
-         dU = 0, Hg = 0, dXs = 0, dg = 0, dz = 0, dxr = 0, total = 0;
+         dU = 0, Hg = 0, dXs = 0, dg = 0, dzp = 0, dzt = 0, wsp = 0, x3 = 0, rg = 0, dxr = 0,
+         total = 0;
+  int Ep = 0;  // experts padded to a multiple of 64 (router-gradient planes)
 };
 
 BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
@@ -127,7 +129,12 @@ BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
   B.Hg = take((size_t)S * I * 2);
   B.dXs = take((size_t)S * d * 4);
   B.dg = take((size_t)T * K * 4);
-  B.dz = take((size_t)T * E * 4);
+  B.Ep = (int)((E + 63) / 64 * 64);
+  B.dzp = take((size_t)T * 6 * B.Ep * 2);
+  B.dzt = take((size_t)3 * T * B.Ep * 2);
+  B.wsp = take((size_t)6 * B.Ep * d * 2);
+  B.x3 = take((size_t)3 * T * d * 2);
+  B.rg = take(64);
   B.dxr = take((size_t)T * d * 4);
   B.total = off;
   return B;
@@ -413,9 +420,11 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
   const int N = shape->n_ffn, d = shape->d_model, I = shape->d_expert, K = shape->top_k;
   const int E = (int)n_experts(*shape);
-  // the grouped GEMMs address one expert's slot rows (up to T of them) with
-  // 32-bit byte offsets
-  if ((long long)T * std::max(d, 2 * I) * 2 >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
+  // the grouped GEMMs address one expert's slot rows (up to T of them), and
+  // the router-gradient planes of T tokens, with 32-bit byte offsets
+  const long long Ep = (E + 63) / 64 * 64;
+  if ((long long)T * std::max<long long>(std::max(d, 2 * I), 6 * Ep) * 2 >= (1ll << 32))
+    return LCMOE_ERR_UNSUPPORTED;
   if (T == 0) {  // no tokens: every gradient is zero
     if (hipMemsetAsync(dw_router, 0, (size_t)E * d * 4, stream) != hipSuccess ||
         hipMemsetAsync(dw13, 0, (size_t)N * 2 * I * d * 2, stream) != hipSuccess ||
@@ -451,7 +460,8 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   uint16_t* Hg = at<uint16_t>(base, B.Hg);
   float* dXs = at<float>(base, B.dXs);
   float* dg = at<float>(base, B.dg);
-  float* dz = at<float>(base, B.dz);
+  uint16_t* dzp = at<uint16_t>(base, B.dzp);
+  uint16_t* dzt = at<uint16_t>(base, B.dzt);
   float* dxr = at<float>(base, B.dxr);
   const int* s_dev = at<int>(base, L.meta) + 2;  // FFN slot count
 
@@ -494,7 +504,7 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   // 4. per slot row: dg, dU, g*h; zero-slot dg; router dz
   launch_bwd_rows(U, Q, perm, gate, s_dev, I, dU, Hg, dg, row_grid, stream);
   launch_bwd_zero_dg(x, dy, idx, T, d, K, N, dg, stream);
-  launch_bwd_router_dz(logits, idx, gate, dg, T, E, K, dz, stream);
+  launch_bwd_router_dz(logits, idx, gate, dg, T, E, B.Ep, K, dzp, dzt, stream);
   mark(ev, 4, stream);
 
   // 5. dX per slot row = dU_e W13_e (W13 read k-major)
@@ -507,19 +517,22 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   // 6. dW2_e[c][j] = sum over the expert's slots of dy[t][c] (g h)[s][j]
   g.a = dYs; g.a_ld = d;
   g.b = Hg; g.b_ld = I; g.b_estride = 0;
-  g.c = dw2; g.c_ld = I; g.M = d; g.N = I;
+  g.c = dw2; g.c_ld = I; g.M = d; g.m_store = d; g.N = I;
   launch_bwd_wgrad(g, bwd_wgrad_grid(N, d, I), stream);
   mark(ev, 6, stream);
 
   // 7. dW13_e[r][c] = sum over the expert's slots of dU[s][r] x[t][c]
   g.a = dU; g.a_ld = 2 * I;
   g.b = Xs; g.b_ld = d;
-  g.c = dw13; g.c_ld = d; g.M = 2 * I; g.N = d;
+  g.c = dw13; g.c_ld = d; g.M = 2 * I; g.m_store = 2 * I; g.N = d;
   launch_bwd_wgrad(g, bwd_wgrad_grid(N, 2 * I, d), stream);
   mark(ev, 7, stream);
 
-  // 8. router: dW_r = dz^T x, dx_r = dz W_r (fp32)
-  launch_router_grads(dz, x, w_router, T, E, d, dw_router, dxr, stream);
+  // 8. router: dW_r = dz^T x, dx_r = dz W_r on bf16 MFMA from exact planes of dz
+  //    and W_r (fp32 accumulation)
+  if (!launch_router_grads(dzp, dzt, x, w_router, T, E, B.Ep, d, at<uint16_t>(base, B.wsp),
+                           at<uint16_t>(base, B.x3), at<int>(base, B.rg), dw_router, dxr, stream))
+    return LCMOE_ERR_HIP;
   mark(ev, 8, stream);
 
   // 9. dx

@@ -29,17 +29,6 @@ namespace lcmoe {
 // ---------------------------------------------------------------------------
 constexpr int RBM = 256, RBN = 128, RBK = 32;
 
-__device__ __forceinline__ void split3(float w, uint16_t& h, uint16_t& m, uint16_t& l) {
-  __bf16 bh = (__bf16)w;
-  float r1 = w - (float)bh;
-  __bf16 bm = (__bf16)r1;
-  float r2 = r1 - (float)bm;
-  __bf16 bl = (__bf16)r2;
-  h = *reinterpret_cast<uint16_t*>(&bh);
-  m = *reinterpret_cast<uint16_t*>(&bm);
-  l = *reinterpret_cast<uint16_t*>(&bl);
-}
-
 __device__ __forceinline__ int rswz(int row, int chunk) {
   return row * 4 + (chunk ^ ((row >> 2) & 3));
 }
