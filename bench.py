@@ -334,7 +334,9 @@ def backward_work(cfg, counts, T):
     c = counts[:N].astype(np.int64)
     S, et = int(c.sum()), int((c > 0).sum())
     w13, w2 = 2 * I * d * 2, d * I * 2
+    Ep = (E + 63) // 64 * 64
     return {
+        "route_gather": dict(bytes=T * d * 2 + E * d * 4 + T * E * 4 + 2 * S * d * 2 * 2, flops=0.0),
         "u": dict(bytes=et * w13 + S * (d * 2 + 2 * I * 4), flops=2.0 * S * 2 * I * d),
         "w2t_dy": dict(bytes=et * w2 + S * (d * 2 + I * 4), flops=2.0 * S * I * d),
         "rows_router": dict(bytes=S * (2 * I * 4 + I * 4 + 2 * I * 2 + I * 2) + 2 * T * E * 4,
@@ -342,6 +344,7 @@ def backward_work(cfg, counts, T):
         "dx_rows": dict(bytes=et * w13 + S * (2 * I * 2 + d * 4), flops=2.0 * S * 2 * I * d),
         "dw2": dict(bytes=N * w2 + S * (d * 2 + I * 2), flops=2.0 * S * d * I),
         "dw13": dict(bytes=N * w13 + S * (2 * I * 2 + d * 2), flops=2.0 * S * 2 * I * d),
+        # algorithmic: the fp32 GEMMs dz^T x and dz W_r (the MFMA runs 18 T Ep d on planes)
         "router_grads": dict(bytes=T * E * 4 + T * d * 2 + 2 * E * d * 4 + T * d * 4,
                              flops=4.0 * T * E * d),
         "dx": dict(bytes=S * d * 4 + T * d * (2 + 4 + 4), flops=0.0),

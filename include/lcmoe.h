@@ -221,7 +221,8 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
  * The routing and the expert pre-activations u are recomputed from x (the
  * same kernels as the forward, so the same selection). bf16 weights only.
  * Expert GEMMs: bf16 operands (u and W2^T dy kept in fp32, du and g h
- * rounded to bf16), fp32 accumulation; router gradients in fp32.
+ * rounded to bf16), fp32 accumulation; router gradients at fp32 accuracy
+ * (bf16 MFMA on exact three-plane splits of dz and W_r, fp32 accumulation).
  *
  *   x_bf16, w_router, bias, w13, w2   as for lcmoe_forward (read)
  *   dy_bf16    [T][d] bf16 device, read: gradient of the loss w.r.t. y
