@@ -81,6 +81,27 @@ def stage_of_kernel(name):
     return None
 
 
+BWD_OPS = {1: "u", 2: "w2t_dy", 3: "dx_rows", 4: "dw2", 5: "dw13", 6: "router_grads",
+           7: "router_grads"}
+
+
+def bwd_stage_of_kernel(name):
+    """Map a kernel symbol of a backward-only run to its backward stage."""
+    if "bwd_gemm_kernel<" in name:
+        op = int(name.split("bwd_gemm_kernel<")[1].split(">")[0].split(",")[-1])
+        return BWD_OPS.get(op)
+    for key, stage in (("gather_rows", "route_gather"), ("router_gemm", "route_gather"),
+                       ("topk", "route_gather"), ("hist_kernel", "route_gather"),
+                       ("colscan", "route_gather"), ("schedule_kernel", "route_gather"),
+                       ("scatter", "route_gather"), ("tile_prefix", "route_gather"),
+                       ("bwd_rows", "rows_router"), ("bwd_zero_dg", "rows_router"),
+                       ("bwd_router_dz", "rows_router"), ("router_w_split", "router_grads"),
+                       ("bwd_dx", "dx")):
+        if key in name:
+            return stage
+    return None
+
+
 def measured_traffic(workload, stage):
     """HBM bytes per launch of `stage` from profiles/traffic.json, or None if
     absent or taken on different kernel sources."""
@@ -155,6 +176,7 @@ def trace_summary(trace_dir, workload, cmd, out_path):
     """Write the rocprofv3 --kernel-trace --stats summary of the layer's
     kernels (calls, average / min / max duration) as a markdown table."""
     import csv
+    mapper = bwd_stage_of_kernel if workload.startswith("backward") else stage_of_kernel
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
     lines = [f"# rocprofv3 kernel statistics: {workload} workload", "",
              "Command (from the repository root on the GPU host):", "", "```", cmd, "```", "",
@@ -162,7 +184,7 @@ def trace_summary(trace_dir, workload, cmd, out_path):
              "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
-        st = stage_of_kernel(name)
+        st = mapper(name)
         if st is None and "copyBuffer" not in name:
             continue
         short = name.split("(")[0].replace("void ", "")
@@ -334,7 +356,6 @@ def backward_work(cfg, counts, T):
     c = counts[:N].astype(np.int64)
     S, et = int(c.sum()), int((c > 0).sum())
     w13, w2 = 2 * I * d * 2, d * I * 2
-    Ep = (E + 63) // 64 * 64
     return {
         "route_gather": dict(bytes=T * d * 2 + E * d * 4 + T * E * 4 + 2 * S * d * 2 * 2, flops=0.0),
         "u": dict(bytes=et * w13 + S * (d * 2 + 2 * I * 4), flops=2.0 * S * 2 * I * d),
@@ -482,6 +503,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward measurement on the bf16 prefill batch")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="measure only the backward on the prefill batch (for profiling runs)")
     ap.add_argument("--cpu-experts", type=int, default=160)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="fold rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
@@ -506,6 +529,13 @@ def main():
     lcmoe.lib()  # fail loudly if the HIP library is missing
     assert torch.cuda.is_available(), "no GPU visible"
     hip = _hip()
+    if args.backward_only:
+        cfg = inputs.CONFIGS["prefill"]
+        L = inputs.make_layer(cfg, "cuda")
+        x = inputs.make_tokens(cfg, "cuda")
+        bw = measure_backward(cfg, L, x, args.steps, args.warmup, hip)
+        print(json.dumps({"backward": bw}))
+        return
     copy_gbps = copy_bandwidth()
     print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read+write)", file=sys.stderr, flush=True)
     results = {}

@@ -257,7 +257,7 @@ bool launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_
   g.b = wsp; g.b_ld = d; g.b_estride = 0;
   g.c = dxr; g.c_ld = d; g.N = d; g.K = 6 * Ep;
   g.counts = rg; g.offsets = rg + 1; g.tile_prefix = rg + 2;
-  launch_bwd_dgrad(g, true, true, bwd_dgrad_grid(T, 1, d), s);
+  launch_bwd_dgrad(g, kBwdRouterDx, bwd_dgrad_grid(T, 1, d), s);
   // dW_r[i][c] = sum over the 3 T plane rows of dz[t][i] x[t][c]
   BwdGemmArgs w{};
   w.n_ffn = 1;

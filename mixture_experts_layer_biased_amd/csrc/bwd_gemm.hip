@@ -186,7 +186,8 @@ __device__ __forceinline__ void store_subtile(const f32x16_t (&acc)[2][2], uint4
 
 }  // namespace
 
-template <bool WGRAD, bool B_KM, bool OUT_F32, int WM, int WN, int FM, int FN, int NSLOT>
+// OP (a BwdOp) only names the launch, so profiles tell the GEMMs apart.
+template <bool WGRAD, bool B_KM, bool OUT_F32, int WM, int WN, int FM, int FN, int NSLOT, int OP>
 __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
   constexpr bool A_KM = WGRAD;
   constexpr bool BKM = WGRAD || B_KM;
@@ -424,23 +425,28 @@ int bwd_wgrad_grid(int n_ffn, int M, int N) {
   return (int)std::min<long long>(items + 8, 1ll << 30);
 }
 
-void launch_bwd_dgrad(const BwdGemmArgs& g, bool b_km, bool out_f32, int grid, hipStream_t s) {
+void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
   static_assert(kBwdTileM == 128 && kBwdTileNDgrad == 256, "dgrad tile");
-  if (b_km) {
-    if (out_f32) bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
-    else bwd_gemm_kernel<false, true, false, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
-  } else {
-    if (out_f32) bwd_gemm_kernel<false, false, true, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
-    else bwd_gemm_kernel<false, false, false, 2, 4, 2, 2, 3><<<grid, 512, 0, s>>>(g);
+  switch (op) {
+    case kBwdU: bwd_gemm_kernel<false, false, true, 2, 4, 2, 2, 3, kBwdU><<<grid, 512, 0, s>>>(g); break;
+    case kBwdQ: bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdQ><<<grid, 512, 0, s>>>(g); break;
+    case kBwdDx: bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdDx><<<grid, 512, 0, s>>>(g); break;
+    default:
+      bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdRouterDx><<<grid, 512, 0, s>>>(g);
+      break;
   }
 }
-void launch_bwd_wgrad(const BwdGemmArgs& g, int grid, hipStream_t s) {
-  bwd_gemm_kernel<true, true, false, kWgWM, kWgWN, kWgFM, kWgFN, 2>
-      <<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
+void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
+  if (op == kBwdDw2)
+    bwd_gemm_kernel<true, true, false, kWgWM, kWgWN, kWgFM, kWgFN, 2, kBwdDw2>
+        <<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
+  else
+    bwd_gemm_kernel<true, true, false, kWgWM, kWgWN, kWgFM, kWgFN, 2, kBwdDw13>
+        <<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
 }
 void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s) {
   const long long items = (long long)g.n_ffn * ((g.M + 127) / 128) * ((g.N + 127) / 128);
-  bwd_gemm_kernel<true, true, true, 2, 2, 2, 2, 3>
+  bwd_gemm_kernel<true, true, true, 2, 2, 2, 2, 3, kBwdRouterDw>
       <<<(int)std::min<long long>(items + 8, 1ll << 30), 256, 0, s>>>(g);
 }
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,

@@ -87,8 +87,11 @@ struct BwdGemmArgs {
 };
 int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols);
 int bwd_wgrad_grid(int n_ffn, int M, int N);
-void launch_bwd_dgrad(const BwdGemmArgs& g, bool b_km, bool out_f32, int grid, hipStream_t s);
-void launch_bwd_wgrad(const BwdGemmArgs& g, int grid, hipStream_t s);
+// The backward's grouped GEMMs (dgrad: U = X W13^T with W13 k-contiguous, the
+// others read their weight k-major; wgrad: the weight gradients).
+enum BwdOp { kBwdU = 1, kBwdQ, kBwdDx, kBwdDw2, kBwdDw13, kBwdRouterDx, kBwdRouterDw };
+void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s);
+void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s);
 // wgrad with fp32 output and 128 x 128 tiles (the router gradient: few tiles, long k)
 void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s);
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,

@@ -491,14 +491,14 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   g.a = Xs; g.a_ld = d;
   g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
   g.c = U; g.c_ld = 2 * I; g.N = 2 * I; g.K = d;
-  launch_bwd_dgrad(g, false, true, bwd_dgrad_grid(smax, N, 2 * I), stream);
+  launch_bwd_dgrad(g, kBwdU, bwd_dgrad_grid(smax, N, 2 * I), stream);
   mark(ev, 2, stream);
 
   // 3. Q = dY_e W2_e (W2 read k-major), per FFN slot row
   g.a = dYs; g.a_ld = d;
   g.b = static_cast<const uint16_t*>(w2); g.b_ld = I; g.b_estride = (long long)d * I;
   g.c = Q; g.c_ld = I; g.N = I; g.K = d;
-  launch_bwd_dgrad(g, true, true, bwd_dgrad_grid(smax, N, I), stream);
+  launch_bwd_dgrad(g, kBwdQ, bwd_dgrad_grid(smax, N, I), stream);
   mark(ev, 3, stream);
 
   // 4. per slot row: dg, dU, g*h; zero-slot dg; router dz
@@ -511,21 +511,21 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   g.a = dU; g.a_ld = 2 * I;
   g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
   g.c = dXs; g.c_ld = d; g.N = d; g.K = 2 * I;
-  launch_bwd_dgrad(g, true, true, bwd_dgrad_grid(smax, N, d), stream);
+  launch_bwd_dgrad(g, kBwdDx, bwd_dgrad_grid(smax, N, d), stream);
   mark(ev, 5, stream);
 
   // 6. dW2_e[c][j] = sum over the expert's slots of dy[t][c] (g h)[s][j]
   g.a = dYs; g.a_ld = d;
   g.b = Hg; g.b_ld = I; g.b_estride = 0;
   g.c = dw2; g.c_ld = I; g.M = d; g.m_store = d; g.N = I;
-  launch_bwd_wgrad(g, bwd_wgrad_grid(N, d, I), stream);
+  launch_bwd_wgrad(g, kBwdDw2, bwd_wgrad_grid(N, d, I), stream);
   mark(ev, 6, stream);
 
   // 7. dW13_e[r][c] = sum over the expert's slots of dU[s][r] x[t][c]
   g.a = dU; g.a_ld = 2 * I;
   g.b = Xs; g.b_ld = d;
   g.c = dw13; g.c_ld = d; g.M = 2 * I; g.m_store = 2 * I; g.N = d;
-  launch_bwd_wgrad(g, bwd_wgrad_grid(N, 2 * I, d), stream);
+  launch_bwd_wgrad(g, kBwdDw13, bwd_wgrad_grid(N, 2 * I, d), stream);
   mark(ev, 7, stream);
 
   // 8. router: dW_r = dz^T x, dx_r = dz W_r on bf16 MFMA from exact planes of dz
