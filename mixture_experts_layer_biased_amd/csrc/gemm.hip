@@ -497,8 +497,16 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[j][i], Bv[j][0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[j][i], Bv[j][1], acc[i][1], 0, 0, 0);
+        // bf16 weights: transposed tile (weights as the first operand, lane =
+        // token row) for the LDS-staged epilogue; fp8 weights: direct tile
+        // (lane = output column), which measured faster there.
+        if (!FP8) {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bv[j][0], Av[j][i], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bv[j][1], Av[j][i], acc[i][1], 0, 0, 0);
+        } else {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[j][i], Bv[j][0], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Av[j][i], Bv[j][1], acc[i][1], 0, 0, 0);
+        }
       }
   };
   // Stage s: wait for its copies (younger stages stay in flight), publish,
@@ -523,24 +531,74 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
     default: kloop(std::integral_constant<int, 0>{}); break;
   }
 
+  if (FP8) {
+    // fp8 weights, direct tile: lane = output column, 16 rows per fragment.
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      if (frow(i) >= rows) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tr = frow(i) + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (tr >= rows) continue;
+        uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
+        if (GATEUP) {
+          const int col = slice * kBigColsGateUp + 32 * wn + (lane & 31);
+          if (col < a.n_out) orow[col] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+        } else {
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const int col = slice * kBigColsDown + 64 * wn + 32 * f + (lane & 31);
+            if (col < a.n_out) orow[col] = f32_to_bf16(acc[i][f][v]);
+          }
+        }
+      }
+    }
+    return;
+  }
+  // bf16 weights. The accumulators hold the transposed tile: lane l has token row
+  // frow(i) + l % 32 and, per fragment, the 4 consecutive output columns
+  // 8 q + 4 (l / 32) + [0, 4) for q = 0..3. Each 32-row fragment goes out
+  // through this wave's 4 KB of LDS (the ring is free after the barrier), so
+  // a global store instruction writes whole row segments of the wave's
+  // columns: 128 bytes (down, 64 columns) or 64 bytes (gate/up, 32 columns).
+  // Row r's 16-byte chunk c sits at c ^ ((r >> 1) & 7) (down, 8 chunks per
+  // row) or c ^ ((r >> 2) & 3) (gate/up, 4 chunks): conflict-free both ways.
+  raw_barrier();
+  constexpr int CPR = GATEUP ? 4 : 8;  // 16-byte chunks per staged row
+  uint4* st = lds + wave * 256;
+  auto sw_of = [&](int r) { return GATEUP ? ((r >> 2) & 3) : ((r >> 1) & 7); };
+  const int col0 = GATEUP ? slice * kBigColsGateUp + 32 * wn : slice * kBigColsDown + 64 * wn;
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     if (frow(i) >= rows) continue;
+    const int r = lane & 31;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tr = frow(i) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (tr >= rows) continue;
-      uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
+    for (int q = 0; q < 4; ++q) {
       if (GATEUP) {
-        const int col = slice * kBigColsGateUp + 32 * wn + (lane & 31);
-        if (col < a.n_out) orow[col] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+        const f32x16_t& g = acc[i][0];
+        const f32x16_t& u = acc[i][1];
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(st + r * CPR + (q ^ sw_of(r))) + 8 * h) =
+            make_uint2(pack_bf16x2(silu_f(g[4 * q]) * u[4 * q], silu_f(g[4 * q + 1]) * u[4 * q + 1]),
+                       pack_bf16x2(silu_f(g[4 * q + 2]) * u[4 * q + 2],
+                                   silu_f(g[4 * q + 3]) * u[4 * q + 3]));
       } else {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int col = slice * kBigColsDown + 64 * wn + 32 * f + (lane & 31);
-          if (col < a.n_out) orow[col] = f32_to_bf16(acc[i][f][v]);
+          const f32x16_t& y = acc[i][f];
+          const int c = 4 * f + q;
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(st + r * CPR + (c ^ sw_of(r))) + 8 * h) =
+              make_uint2(pack_bf16x2(y[4 * q], y[4 * q + 1]), pack_bf16x2(y[4 * q + 2], y[4 * q + 3]));
         }
       }
+    }
+    constexpr int RPI = 64 / CPR;  // rows per read instruction
+#pragma unroll
+    for (int j = 0; j < 32 / RPI; ++j) {
+      const int rr = RPI * j + lane / CPR, c = lane % CPR;
+      const uint4 v = st[rr * CPR + (c ^ sw_of(rr))];
+      const int tr = frow(i) + rr, col = col0 + 8 * c;
+      if (tr < rows && col < a.n_out)
+        *reinterpret_cast<uint4*>(a.out + (size_t)(rowbase + tr) * a.n_out + col) = v;
     }
   }
 }
@@ -723,8 +781,9 @@ __global__ __launch_bounds__(512) void gemm_big_a8_kernel(GemmArgs a) {
         f32x16_t t;
 #pragma unroll
         for (int v = 0; v < 16; ++v) t[v] = 0.f;
-        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av[0], Bv[0][f], t, 0, 0, 0, 127, 0, 127);
-        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av[1], Bv[1][f], t, 0, 0, 0, 127, 0, 127);
+        // transposed tile (weights as the first operand): lane = token row
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Bv[0][f], Av[0], t, 0, 0, 0, 127, 0, 127);
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Bv[1][f], Av[1], t, 0, 0, 0, 127, 0, 127);
         const float sc = f ? s1 : s0;
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][f][v] = __builtin_fmaf(t[v], sc, acc[i][f][v]);
@@ -750,25 +809,35 @@ __global__ __launch_bounds__(512) void gemm_big_a8_kernel(GemmArgs a) {
   }
 
   // Epilogue: the per-row activation scale, then SiLU-gating (gate/up) or
-  // the store of Y (down).
+  // the store of Y (down). Transposed tile as in the bf16 kernel: lane =
+  // token row, 4 consecutive output columns per fragment and q.
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
-    if (frow(i) >= rows) continue;
+    const int tr = frow(i) + lrow;
+    if (frow(i) >= rows || tr >= rows) continue;
+    const float sa = GATEUP ? a.ascale[a.perm[rowbase + tr] / a.topk] : a.ascale[rowbase + tr];
+    uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tr = frow(i) + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (tr >= rows) continue;
-      const float sa = GATEUP ? a.ascale[a.perm[rowbase + tr] / a.topk] : a.ascale[rowbase + tr];
-      uint16_t* orow = a.out + (size_t)(rowbase + tr) * a.n_out;
+    for (int q = 0; q < 4; ++q) {
       if (GATEUP) {
-        const int col = slice * kBigColsGateUp + 32 * wn + lrow;
-        if (col < a.n_out)
-          orow[col] = f32_to_bf16(silu_f(acc[i][0][v] * sa) * (acc[i][1][v] * sa));
+        const int col = slice * kBigColsGateUp + 32 * wn + 8 * q + 4 * h;
+        if (col < a.n_out) {
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            o[r] = silu_f(acc[i][0][4 * q + r] * sa) * (acc[i][1][4 * q + r] * sa);
+          *reinterpret_cast<uint2*>(orow + col) =
+              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        }
       } else {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int col = slice * kBigColsDown + 64 * wn + 32 * f + lrow;
-          if (col < a.n_out) orow[col] = f32_to_bf16(acc[i][f][v] * sa);
+          const int col = slice * kBigColsDown + 64 * wn + 32 * f + 8 * q + 4 * h;
+          const f32x16_t& y = acc[i][f];
+          if (col < a.n_out)
+            *reinterpret_cast<uint2*>(orow + col) =
+                make_uint2(pack_bf16x2(y[4 * q] * sa, y[4 * q + 1] * sa),
+                           pack_bf16x2(y[4 * q + 2] * sa, y[4 * q + 3] * sa));
         }
       }
     }
