@@ -188,7 +188,7 @@ def trace_summary(trace_dir, workload, cmd, out_path):
         if st is None and "copyBuffer" not in name:
             continue
         short = name.split("(")[0].replace("void ", "")
-        lines.append(f"| `{short}` | {st or 'device copies (weight setup + 4 GiB calibration)'} | {r['Calls']} | "
+        lines.append(f"| `{short}` | {st or 'device copies (setup, calibration, backward x copies)'} | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     with open(out_path, "w") as f:
