@@ -208,6 +208,16 @@ def make_event_sets(hip, n_sets, n_events):
     return sets
 
 
+def step_ms(hip, sets, n_stages):
+    """Per-step duration (first to last stage event) of every timed step."""
+    out = []
+    for arr in sets:
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), arr[0], arr[n_stages]) == 0
+        out.append(ms.value)
+    return np.array(out)
+
+
 def stage_ms(hip, sets, n_stages):
     out = np.zeros((len(sets), n_stages))
     for s, arr in enumerate(sets):
@@ -285,6 +295,7 @@ def measure(cfg, steps, warmup, hip):
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     per_stage = stage_ms(hip, sets, nst)
+    per_step = step_ms(hip, sets, nst)
     for arr in sets:
         for i in range(nst + 1):
             hip.hipEventDestroy(arr[i])
@@ -308,6 +319,7 @@ def measure(cfg, steps, warmup, hip):
     lb = layer_bytes(cfg, counts, T)
     res = dict(
         tokens=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), wall_s=wall,
+        step_ms_median=float(np.median(per_step)), step_ms_min=float(per_step.min()),
         mean_ffn_experts_per_token=float(counts[: cfg.n_ffn].sum() / T),
         touched_experts=int((counts[: cfg.n_ffn] > 0).sum()),
         max_rows_per_expert=int(counts[: cfg.n_ffn].max()),

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
   constexpr int JA = (A_CH / 64) / NW;         // the first JA of them fill A
   static_assert(NB % NW == 0 && (A_CH / 64) % NW == 0, "copy blocks must split evenly");
   static_assert(NW * (OUT_F32 ? 1024 : 512) <= NSLOT * SLOT, "epilogue staging fits in the ring");
-  static_assert((NSLOT - 2) * (NB / NW) <= 63, "vmcnt range");
+  static_assert((NSLOT - 1) * (NB / NW) <= 24, "vmcnt range of the waits");
   static_assert(!A_KM || BM % 128 == 0, "i-contiguous tiles are 128 wide");
   static_assert(!BKM || BN % 128 == 0, "i-contiguous tiles are 128 wide");
   __shared__ uint4 lds[NSLOT * SLOT];
@@ -365,11 +365,15 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
     }
   };
 
-  for (int s = 0; s < NSLOT - 1 && s < nst; ++s) issue(s);
+  // Every slot is free at the start, so NSLOT stages go out at once (a tile
+  // of at most NSLOT stages waits for one round trip); from stage 1 on, the
+  // next stage goes into the slot stage s - 1 has just released.
+  int issued = min(NSLOT, nst);
+  for (int s = 0; s < issued; ++s) issue(s);
   for (int s = 0; s < nst; ++s) {
-    bwait_vmcnt_upto(per_stage * min(NSLOT - 2, nst - 1 - s));
+    bwait_vmcnt_upto(per_stage * (issued - 1 - s));
     braw_barrier();
-    if (s + NSLOT - 1 < nst) issue(s + NSLOT - 1);
+    if (s >= 1 && issued < nst) issue(issued++);
     compute(s);
   }
 
