@@ -81,12 +81,13 @@ def stage_of_kernel(name):
     return None
 
 
-BWD_OPS = {1: "u", 2: "w2t_dy", 3: "dx_rows", 4: "dw2", 5: "dw13", 6: "router_grads",
-           7: "router_grads"}
+BWD_OPS = {2: "w2t_dy", 3: "dx_rows", 4: "dw2", 5: "dw13", 6: "router_grads", 7: "router_grads"}
 
 
 def bwd_stage_of_kernel(name):
     """Map a kernel symbol of a backward-only run to its backward stage."""
+    if "gemm_big_dma_kernel<true, false, true>" in name:
+        return "u_silu"
     if "bwd_gemm_kernel<" in name:
         op = int(name.split("bwd_gemm_kernel<")[1].split(">")[0].split(",")[-1])
         return BWD_OPS.get(op)
@@ -94,8 +95,8 @@ def bwd_stage_of_kernel(name):
                        ("topk", "route_gather"), ("hist_kernel", "route_gather"),
                        ("colscan", "route_gather"), ("schedule_kernel", "route_gather"),
                        ("scatter", "route_gather"), ("tile_prefix", "route_gather"),
-                       ("bwd_rows", "rows_router"), ("bwd_zero_dg", "rows_router"),
-                       ("bwd_router_dz", "rows_router"), ("router_w_split", "router_grads"),
+                       ("bwd_dg_reduce", "dz"), ("bwd_zero_dg", "dz"),
+                       ("bwd_router_dz", "dz"), ("router_w_split", "router_grads"),
                        ("bwd_dx", "dx")):
         if key in name:
             return stage
@@ -370,10 +371,11 @@ def backward_work(cfg, counts, T):
     w13, w2 = 2 * I * d * 2, d * I * 2
     return {
         "route_gather": dict(bytes=T * d * 2 + E * d * 4 + T * E * 4 + 2 * S * d * 2 * 2, flops=0.0),
-        "u": dict(bytes=et * w13 + S * (d * 2 + 2 * I * 4), flops=2.0 * S * 2 * I * d),
         "w2t_dy": dict(bytes=et * w2 + S * (d * 2 + I * 4), flops=2.0 * S * I * d),
-        "rows_router": dict(bytes=S * (2 * I * 4 + I * 4 + 2 * I * 2 + I * 2) + 2 * T * E * 4,
-                            flops=0.0),
+        # u = W13 x with the SiLU backward fused: reads Q, writes dU and g h
+        "u_silu": dict(bytes=et * w13 + S * (d * 2 + I * 4 + 2 * I * 2 + I * 2),
+                       flops=2.0 * S * 2 * I * d),
+        "dz": dict(bytes=T * E * 4 + T * E * 6 * 2, flops=0.0),
         "dx_rows": dict(bytes=et * w13 + S * (2 * I * 2 + d * 4), flops=2.0 * S * 2 * I * d),
         "dw2": dict(bytes=N * w2 + S * (d * 2 + I * 2), flops=2.0 * S * d * I),
         "dw13": dict(bytes=N * w13 + S * (2 * I * 2 + d * 2), flops=2.0 * S * 2 * I * d),

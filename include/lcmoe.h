@@ -242,8 +242,8 @@ lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_b
                             hipStream_t stream);
 /* The same call, recording the caller's 10 events (array, may be NULL) at
  * stage boundaries: start, routing (with the gather of each FFN slot's x
- * and dy rows into slot order), u, W2^T dy, per-row/router, dx rows, dW2,
- * dW13, router gradients, dx. */
+ * and dy rows into slot order), W2^T dy, u with the SiLU backward, dg and
+ * the router's dz, dx rows, dW2, dW13, router gradients, dx. */
 lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                                    const float* w_router, const float* bias, const void* w13,
                                    const void* w2, const void* dy_bf16, float* dx,

@@ -9,7 +9,8 @@
 //   dz_t = p_t * (dp_t - <dp_t, p_t>), dp_t[idx_tk] = dg_tk
 //   dx_t = sum_FFN (dU W13)_s + (sum_zero g_tk) dy_t + (dz W_r)_t
 //
-// The expert GEMMs (U, Q, dU W13, the weight gradients) are in bwd_gemm.hip.
+// The expert GEMMs are in bwd_gemm.hip (W2^T dy, dU W13, the weight
+// gradients) and gemm.hip (u = W13 x with the SiLU backward in its epilogue).
 #include <algorithm>
 
 #include "common.h"
@@ -19,7 +20,8 @@ namespace lcmoe {
 
 // prefix[e] = sum_{e' < e} ceil(counts[e'] / rows), one wave (N <= 2048).
 __global__ __launch_bounds__(64) void tile_prefix_kernel(const int* __restrict__ counts, int N,
-                                                         int rows, int* __restrict__ prefix) {
+                                                         int rows, int* __restrict__ prefix,
+                                                         int* __restrict__ total) {
   const int lane = threadIdx.x;
   const int per = (N + 63) / 64;
   const int lo = lane * per, hi = min(N, lo + per);
@@ -31,45 +33,24 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int* __restrict__
     prefix[e] = run;
     run += (counts[e] + rows - 1) / rows;
   }
-  if (lane == 63) prefix[N] = incl;
+  if (lane == 63) {
+    prefix[N] = incl;
+    if (total != nullptr) *total = incl;
+  }
 }
 
-__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + expf(-a)); }
-
-// One wave per FFN slot row s < S (S read on the device): h = silu(a) c from
-// U = [a; c]; dg = <Q_s, h>; dU_s = [dh c silu'(a); dh silu(a)] with
-// dh = g Q_s (bf16); Hg_s = g h (bf16, the dW2 operand).
-__global__ __launch_bounds__(256) void bwd_rows_kernel(const float* __restrict__ U,
-                                                       const float* __restrict__ Q,
-                                                       const int* __restrict__ perm,
-                                                       const float* __restrict__ gate,
-                                                       const int* __restrict__ s_dev, int I,
-                                                       uint16_t* __restrict__ dU,
-                                                       uint16_t* __restrict__ Hg,
-                                                       float* __restrict__ dg) {
-  const int lane = threadIdx.x & 63;
+// One thread per FFN slot row s < S (S read on the device): dg of its slot
+// is the sum of the row's P partials of <Q, h>, in order.
+__global__ __launch_bounds__(256) void bwd_dg_reduce_kernel(const float* __restrict__ dgp, int P,
+                                                            const int* __restrict__ perm,
+                                                            const int* __restrict__ s_dev,
+                                                            float* __restrict__ dg) {
   const int S = *s_dev;
-  const int wpb = blockDim.x >> 6;
-  for (int s = blockIdx.x * wpb + (threadIdx.x >> 6); s < S; s += gridDim.x * wpb) {
-    const int slot = perm[s];
-    const float g = gate[slot];
-    const float* u = U + (size_t)s * 2 * I;
-    const float* q = Q + (size_t)s * I;
-    float part = 0.f;
-    for (int j = lane; j < I; j += 64) {
-      const float a = u[j], c = u[I + j];
-      const float sg = sigmoid_f(a);
-      const float si = a * sg;
-      const float h = si * c;
-      const float qq = q[j];
-      part += qq * h;
-      const float dh = g * qq;
-      dU[(size_t)s * 2 * I + j] = f32_to_bf16(dh * c * (sg * (1.0f + a * (1.0f - sg))));
-      dU[(size_t)s * 2 * I + I + j] = f32_to_bf16(dh * si);
-      Hg[(size_t)s * I + j] = f32_to_bf16(g * h);
-    }
-    part = wave_sum(part);
-    if (lane == 0) dg[slot] = part;
+  for (int s = blockIdx.x * 256 + threadIdx.x; s < S; s += gridDim.x * 256) {
+    const float* p = dgp + (size_t)s * P;
+    float v = 0.f;
+    for (int j = 0; j < P; ++j) v += p[j];
+    dg[perm[s]] = v;
   }
 }
 
@@ -222,13 +203,13 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   }
 }
 
-void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, hipStream_t s) {
-  tile_prefix_kernel<<<1, 64, 0, s>>>(counts, N, rows, prefix);
+void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, int* total,
+                        hipStream_t s) {
+  tile_prefix_kernel<<<1, 64, 0, s>>>(counts, N, rows, prefix, total);
 }
-void launch_bwd_rows(const float* U, const float* Q, const int* perm, const float* gate,
-                     const int* s_dev, int I, uint16_t* dU, uint16_t* Hg, float* dg, int grid,
-                     hipStream_t s) {
-  bwd_rows_kernel<<<grid, 256, 0, s>>>(U, Q, perm, gate, s_dev, I, dU, Hg, dg);
+void launch_bwd_dg_reduce(const float* dgp, int P, const int* perm, const int* s_dev, float* dg,
+                          int grid, hipStream_t s) {
+  bwd_dg_reduce_kernel<<<grid, 256, 0, s>>>(dgp, P, perm, s_dev, dg);
 }
 void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, int T, int d, int K,
                         int N, float* dg, hipStream_t s) {

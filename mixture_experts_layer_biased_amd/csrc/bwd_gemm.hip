@@ -432,7 +432,6 @@ int bwd_wgrad_grid(int n_ffn, int M, int N) {
 void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
   static_assert(kBwdTileM == 128 && kBwdTileNDgrad == 256, "dgrad tile");
   switch (op) {
-    case kBwdU: bwd_gemm_kernel<false, false, true, 2, 4, 2, 2, 3, kBwdU><<<grid, 512, 0, s>>>(g); break;
     case kBwdQ: bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdQ><<<grid, 512, 0, s>>>(g); break;
     case kBwdDx: bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdDx><<<grid, 512, 0, s>>>(g); break;
     default:

@@ -307,8 +307,9 @@ struct DmaTile {
   static constexpr int BG_PER_WAVE = FP8 ? 2 : 4;           // weight copies per wave
 };
 
-template <bool GATEUP, bool FP8>
+template <bool GATEUP, bool FP8, bool BWD = false>
 __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
+  static_assert(!BWD || (GATEUP && !FP8), "the backward epilogue is for bf16 gate/up");
   using TL = DmaTile<FP8>;
   __shared__ uint4 lds[TL::LDS_CHUNKS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -552,6 +553,53 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
           }
         }
       }
+    }
+    return;
+  }
+  if (BWD) {
+    // Backward of the SiLU gate for slot row s = rowbase + tr, columns j of
+    // this lane (a = gate pre-activation, c = up): h = silu(a) c; dh = g Q;
+    // dU = [dh c silu'(a); dh silu(a)]; g h; and <Q, h> over the lane's
+    // columns, summed with the other lane of the row: one partial per row,
+    // slice and wave (32 columns).
+    const int pcount = 4 * a.nslices;
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      if (frow(i) >= rows) continue;
+      const int r = frow(i) + (lane & 31);
+      const bool ok = r < rows;
+      const size_t srow = (size_t)rowbase + (ok ? r : 0);
+      const float g = ok ? a.bgate[a.perm[srow]] : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = slice * kBigColsGateUp + 32 * wn + 8 * q + 4 * h;
+        if (ok && j < a.n_out) {
+          const float4 qv = *reinterpret_cast<const float4*>(a.bq + srow * a.n_out + j);
+          const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+          float da[4], dc[4], hg[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float av = acc[i][0][4 * q + u], cv = acc[i][1][4 * q + u];
+            const float sg = 1.0f / (1.0f + expf(-av));
+            const float si = av * sg;
+            const float hv = si * cv;
+            part += qa[u] * hv;
+            const float dh = g * qa[u];
+            da[u] = dh * cv * (sg * (1.0f + av * (1.0f - sg)));
+            dc[u] = dh * si;
+            hg[u] = g * hv;
+          }
+          uint16_t* du = a.bdu + srow * 2 * a.n_out;
+          *reinterpret_cast<uint2*>(du + j) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+          *reinterpret_cast<uint2*>(du + a.n_out + j) =
+              make_uint2(pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3]));
+          *reinterpret_cast<uint2*>(a.out + srow * a.n_out + j) =
+              make_uint2(pack_bf16x2(hg[0], hg[1]), pack_bf16x2(hg[2], hg[3]));
+        }
+      }
+      part += __shfl_xor(part, 32, kWave);
+      if (ok && h == 0) a.bdgp[srow * pcount + 4 * slice + wn] = part;
     }
     return;
   }
@@ -865,6 +913,10 @@ void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStre
     if (fp8) gemm_big_dma_kernel<false, true><<<grid, 512, 0, s>>>(a);
     else gemm_big_dma_kernel<false, false><<<grid, 512, 0, s>>>(a);
   }
+}
+
+void launch_gemm_big_bwd_u(const GemmArgs& a, int grid, hipStream_t s) {
+  gemm_big_dma_kernel<true, false, true><<<grid, 512, 0, s>>>(a);
 }
 
 void launch_gemm_big_a8(const GemmArgs& a, bool gateup, int grid, hipStream_t s) {

@@ -38,6 +38,15 @@ struct GemmArgs {
   int topk;
   int n_ffn;
   int nslices;             // column blocks per expert
+  // Backward of gate/up (launch_gemm_big_bwd_u only): per slot row s,
+  // Q = W2^T dy [S][I] fp32 and the slot gates (indexed by slot id) are read;
+  // out receives g h (bf16 [S][I]), bdu dU = [dh c silu'(a); dh silu(a)]
+  // (bf16 [S][2I]) and bdgp the partial sums of <Q, h> per 32 columns
+  // (fp32 [S][4 nslices]).
+  const float* bq;
+  const float* bgate;
+  uint16_t* bdu;
+  float* bdgp;
 };
 
 void launch_router(const uint16_t* x, const float* wr, float* zpart, int T, int E, int d,
@@ -50,6 +59,9 @@ void launch_permute(const int* idx, int T, int K, int E, int N, int ntile,
                     int* row_of_slot, hipStream_t s);
 void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
 void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
+// The large-M gate/up GEMM with the backward epilogue (bf16 weights; every
+// expert with slots, M-tiles from mt_prefix, meta[1] = tile count).
+void launch_gemm_big_bwd_u(const GemmArgs& a, int grid, hipStream_t s);
 // Large-M GEMM with fp8 weights and fp8 activations (src8, ascale).
 void launch_gemm_big_a8(const GemmArgs& a, bool gateup, int grid, hipStream_t s);
 // Per-row E4M3FN quantization of bf16 rows: q [rows][cols] codes, scale
@@ -87,19 +99,23 @@ struct BwdGemmArgs {
 };
 int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols);
 int bwd_wgrad_grid(int n_ffn, int M, int N);
-// The backward's grouped GEMMs (dgrad: U = X W13^T with W13 k-contiguous, the
-// others read their weight k-major; wgrad: the weight gradients).
-enum BwdOp { kBwdU = 1, kBwdQ, kBwdDx, kBwdDw2, kBwdDw13, kBwdRouterDx, kBwdRouterDw };
+// The backward's grouped GEMMs on the ring kernel (dgrad, weights read
+// k-major: W2^T dy, dU W13, the router's dz W_r; wgrad: the weight
+// gradients, dW_r).
+enum BwdOp { kBwdQ = 2, kBwdDx, kBwdDw2, kBwdDw13, kBwdRouterDx, kBwdRouterDw };
 void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s);
 void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s);
 // wgrad with fp32 output and 128 x 128 tiles (the router gradient: few tiles, long k)
 void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s);
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,
                         int topk, int d, uint16_t* xs, uint16_t* dys, int grid, hipStream_t s);
-void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, hipStream_t s);
-void launch_bwd_rows(const float* U, const float* Q, const int* perm, const float* gate,
-                     const int* s_dev, int I, uint16_t* dU, uint16_t* Hg, float* dg, int grid,
-                     hipStream_t s);
+// prefix[e] = sum_{e' < e} ceil(counts[e'] / rows), prefix[N] the total,
+// also written to *total when total is not null.
+void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, int* total,
+                        hipStream_t s);
+// dg of the FFN slots: dg[perm[s]] = sum over the P partials of row s, in order.
+void launch_bwd_dg_reduce(const float* dgp, int P, const int* perm, const int* s_dev, float* dg,
+                          int grid, hipStream_t s);
 void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, int T, int d, int K,
                         int N, float* dg, hipStream_t s);
 void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate, const float* dg,

@@ -99,9 +99,10 @@ Layout make_layout(const lcmoe_shape& s, int T) {
 // layout, then the backward's own buffers (S = T * min(K, N) slot rows).
 struct BwdLayout {
   Layout f;
-  size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, Xs = 0, dYs = 0, U = 0, Q = 0,
-         dU = 0, Hg = 0, dXs = 0, dg = 0, dzp = 0, dzt = 0, wsp = 0, x3 = 0, rg = 0, dxr = 0,
-         total = 0;
+  size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, bprefix = 0, bmeta = 0, Xs = 0,
+         dYs = 0, Q = 0, dU = 0, Hg = 0, dgp = 0, dXs = 0, dg = 0, dzp = 0, dzt = 0, wsp = 0, x3 = 0,
+         rg = 0, dxr = 0, total = 0;
+  int nslices = 0;  // 128-column blocks of the gate/up pass (dg partials per row: 4 per block)
   int Ep = 0;  // experts padded to a multiple of 64 (router-gradient planes)
 };
 
@@ -121,12 +122,15 @@ BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
   B.counts = take((size_t)E * 4);
   B.logits = take((size_t)T * E * 4);
   B.tprefix = take((size_t)(N + 1) * 4);
+  B.bprefix = take((size_t)(N + 1) * 4);
+  B.bmeta = take(16);
   B.Xs = take((size_t)S * d * 2);
   B.dYs = take((size_t)S * d * 2);
-  B.U = take((size_t)S * 2 * I * 4);
   B.Q = take((size_t)S * I * 4);
   B.dU = take((size_t)S * 2 * I * 2);
   B.Hg = take((size_t)S * I * 2);
+  B.nslices = (int)((I + kBigColsGateUp - 1) / kBigColsGateUp);
+  B.dgp = take((size_t)S * 4 * B.nslices * 4);
   B.dXs = take((size_t)S * d * 4);
   B.dg = take((size_t)T * K * 4);
   B.Ep = (int)((E + 63) / 64 * 64);
@@ -454,7 +458,6 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   int* tprefix = at<int>(base, B.tprefix);
   uint16_t* Xs = at<uint16_t>(base, B.Xs);
   uint16_t* dYs = at<uint16_t>(base, B.dYs);
-  float* U = at<float>(base, B.U);
   float* Q = at<float>(base, B.Q);
   uint16_t* dU = at<uint16_t>(base, B.dU);
   uint16_t* Hg = at<uint16_t>(base, B.Hg);
@@ -475,7 +478,9 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
                  at<int>(base, L.tilecnt), at<int>(base, L.tileoff), counts, offsets,
                  at<int>(base, L.small_list), at<int>(base, L.mt_prefix), at<int>(base, L.meta),
                  perm, row_of_slot, stream);
-  launch_tile_prefix(counts, N, kBwdTileM, tprefix, stream);
+  launch_tile_prefix(counts, N, kBwdTileM, tprefix, nullptr, stream);
+  int* bmeta = at<int>(base, B.bmeta);
+  launch_tile_prefix(counts, N, kBigTileRows, at<int>(base, B.bprefix), bmeta + 1, stream);
   const long long smax = L.smax;
   const int row_grid = (int)std::min<long long>(4096, (smax + 3) / 4);
   launch_gather_rows(x, dy, perm, s_dev, K, d, Xs, dYs, row_grid, stream);
@@ -487,22 +492,46 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   g.tile_prefix = tprefix;
   g.n_ffn = N;
 
-  // 2. U = X_e W13_e^T (pre-activations, fp32), per FFN slot row
-  g.a = Xs; g.a_ld = d;
-  g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
-  g.c = U; g.c_ld = 2 * I; g.N = 2 * I; g.K = d;
-  launch_bwd_dgrad(g, kBwdU, bwd_dgrad_grid(smax, N, 2 * I), stream);
-  mark(ev, 2, stream);
-
-  // 3. Q = dY_e W2_e (W2 read k-major), per FFN slot row
+  // 2. Q = dY_e W2_e (W2 read k-major), per FFN slot row
   g.a = dYs; g.a_ld = d;
   g.b = static_cast<const uint16_t*>(w2); g.b_ld = I; g.b_estride = (long long)d * I;
   g.c = Q; g.c_ld = I; g.N = I; g.K = d;
   launch_bwd_dgrad(g, kBwdQ, bwd_dgrad_grid(smax, N, I), stream);
+  mark(ev, 2, stream);
+
+  // 3. u = W13_e x per FFN slot row on the forward's large-M gate/up GEMM
+  //    (every expert with slots, M-tiles of up to kBigTileRows rows), with the
+  //    SiLU backward in its epilogue: g h, dU and the partials of dg = <Q, h>
+  {
+    GemmArgs ga{};
+    ga.w = w13;
+    ga.src = x;
+    ga.perm = perm;
+    ga.offsets = offsets;
+    ga.counts = counts;
+    ga.mt_prefix = at<int>(base, B.bprefix);
+    ga.meta = bmeta;
+    ga.out = Hg;
+    ga.kdim = d;
+    ga.n_out = I;
+    ga.rows_total = 2 * I;
+    ga.topk = K;
+    ga.n_ffn = N;
+    ga.nslices = B.nslices;
+    ga.bq = Q;
+    ga.bgate = gate;
+    ga.bdu = dU;
+    ga.bdgp = at<float>(base, B.dgp);
+    const long long tiles_ub = smax / kBigTileRows + std::min<long long>(N, smax);
+    const long long grid = std::max<long long>(8, (tiles_ub * B.nslices + 7) / 8 * 8);
+    launch_gemm_big_bwd_u(ga, (int)std::min<long long>(grid, 1ll << 30), stream);
+  }
   mark(ev, 3, stream);
 
-  // 4. per slot row: dg, dU, g*h; zero-slot dg; router dz
-  launch_bwd_rows(U, Q, perm, gate, s_dev, I, dU, Hg, dg, row_grid, stream);
+  // 4. dg of the FFN slots (sum of the partials) and of the zero slots;
+  //    router dz
+  launch_bwd_dg_reduce(at<float>(base, B.dgp), 4 * B.nslices, perm, s_dev, dg,
+                       (int)std::min<long long>(4096, (smax + 255) / 256), stream);
   launch_bwd_zero_dg(x, dy, idx, T, d, K, N, dg, stream);
   launch_bwd_router_dz(logits, idx, gate, dg, T, E, B.Ep, K, dzp, dzt, stream);
   mark(ev, 4, stream);

@@ -236,7 +236,7 @@ def router_stats(shape, x, logits, counts, n_groups, k_e, alpha=1.0, lam=1.0, ws
 
 
 NUM_BWD_STAGES = 9
-BWD_STAGES = ("route_gather", "u", "w2t_dy", "rows_router", "dx_rows", "dw2", "dw13", "router_grads",
+BWD_STAGES = ("route_gather", "w2t_dy", "u_silu", "dz", "dx_rows", "dw2", "dw13", "router_grads",
               "dx")
 
 

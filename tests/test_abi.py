@@ -213,7 +213,8 @@ def test_backward_workspace(dims):
         n = lcmoe.backward_workspace_bytes(s, T)
         assert n >= prev, (T, n, prev)
         prev = n
-    # the fp32 slot-row intermediates U, Q, dX_s and the bf16 dU, g*h
+    # per slot row: the gathered x and dy rows, the fp32 Q and dX rows, the
+    # bf16 dU and g*h rows
     S = 8192 * min(K, N)
-    assert lcmoe.backward_workspace_bytes(s, 8192) >= S * (2 * I * 4 + I * 4 + d * 4 + 2 * I * 2
+    assert lcmoe.backward_workspace_bytes(s, 8192) >= S * (4 * d + I * 4 + d * 4 + 2 * I * 2
                                                            + I * 2)
