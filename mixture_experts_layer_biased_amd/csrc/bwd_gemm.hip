@@ -5,19 +5,22 @@
 //
 // Two modes:
 //   dgrad: M = the expert's slot count. A is a matrix of slot rows stored
-//     k-contiguous (the gathered x or dy rows, or dU); B is the expert's
-//     weight matrix, k-contiguous (W13 for U = X W13^T) or i-contiguous (W2
-//     for W2^T dy, W13 for dU W13). Output rows are slot rows.
+//     k-contiguous (the gathered dy rows, or dU); B is the expert's weight
+//     matrix read i-contiguous (W2 for W2^T dy, W13 for dU W13; the
+//     k-contiguous form is supported too). Output rows are slot rows. The
+//     router's dz W_r runs in this mode as one group of T rows.
 //   wgrad: K = the expert's slot count. A and B are slot-row matrices read
 //     i-contiguous (element (i, k) at row k, column i): dW2 = dY^T (g h),
 //     dW13 = dU^T X. Output rows are rows of the expert's gradient matrix;
-//     an expert without slots gets zeros.
+//     an expert without slots gets zeros. The router's dz^T x runs in this
+//     mode as one group of 3T plane rows.
 //
 // Tiles of BM x BN (per wave FM x FN fragments of 32 x 32), k stages of 64
 // moved HBM/L2 -> LDS by global_load_lds_dwordx4 (one instruction fills
 // 1 KB of LDS) in a ring of NSLOT stages, as in the forward's large-M kernel:
-// per stage, wait for this wave's copies of the stage, a raw barrier, queue
-// the stage NSLOT-1 ahead into the slot just freed, multiply.
+// all slots are filled at the start of a tile; per stage, wait for this
+// wave's copies of the stage, a raw barrier, queue the next stage into the
+// slot just freed, multiply.
 //
 // LDS tile forms, both conflict-free for 16-lane groups:
 //   k-contiguous [rows][64 k]: 128-byte rows, chunk c of row r at
@@ -26,8 +29,8 @@
 //     row k at w ^ (k & 3); operands read with ds_read_b64_tr_b16, the gfx950
 //     transposing LDS load, which gives each lane 4 consecutive k of one i.
 // The MFMA computes the transposed tile (B as its first operand), so a lane
-// holds 4 consecutive output columns of one row: 16-byte (fp32) or 8-byte
-// (bf16) stores.
+// holds 4 consecutive output columns of one row; each wave's 64 x 64
+// sub-tiles go out through LDS as whole-row stores.
 //
 // Work items are laid out per XCD (blockIdx % 8): each XCD takes a
 // contiguous run of (expert, n tile, m tile) (dgrad) or (expert, m tile,
@@ -194,6 +197,7 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;  // wave tile (32 FM) x (32 FN)
   static_assert(FM % 2 == 0 && FN % 2 == 0, "stores go by 64 x 64 sub-tiles");
+  static_assert(WGRAD || BM == kBwdTileM, "dgrad M tiles are those of the tile prefix");
   constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per stage
   constexpr int SLOT = A_CH + B_CH;
   constexpr int NB = SLOT / 64;                // 1 KB copy blocks per stage
