@@ -512,7 +512,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "fp8", "fp8a8", "prefill32k"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "fp8", "fp8a8", "prefill32k", "ep8_shard"],
+                    default=None,
                     help="measure a single configuration (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
@@ -554,7 +555,8 @@ def main():
     print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read+write)", file=sys.stderr, flush=True)
     results = {}
     baseline = None
-    names = [args.only] if args.only else ["prefill", "decode", "fp8", "fp8a8", "prefill32k"]
+    names = [args.only] if args.only else ["prefill", "decode", "fp8", "fp8a8", "prefill32k",
+                                           "ep8_shard"]
     for name in names:
         cfg = inputs.CONFIGS[name]
         res, keep = measure(cfg, args.steps, args.warmup, hip)

@@ -68,6 +68,12 @@ CONFIGS = {
     # at which the bf16 grouped GEMM has more MFMA work than weight bytes
     # (512 FLOP/B). An extra measurement point, not one of the five above.
     "prefill32k": LayerConfig("prefill32k", 6144, 512, 256, 12, 2048, 32768, seed=6),
+    # One GPU's share of 8-way expert parallelism at the prefill batch: the 64
+    # FFN experts of one rank and the 65,536 FFN slot rows it receives when 8
+    # ranks route 8192 tokens each (about 1024 rows per local expert). Zero
+    # experts never leave a token's home rank, so the shard has none; K = 8
+    # FFN slots per token over 64 experts gives the same rows per expert.
+    "ep8_shard": LayerConfig("ep8_shard", 6144, 64, 0, 8, 2048, 8192, seed=7),
 }
 
 

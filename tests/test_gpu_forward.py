@@ -92,7 +92,7 @@ def _sample(x, n, extra_large=0):
 
 @pytest.mark.parametrize("name,n_sample,n_skew", [("decode", 8, 0), ("prefill", 6, 2),
                                                   ("fp8", 5, 0), ("fp8a8", 5, 0),
-                                                  ("prefill32k", 4, 0)])
+                                                  ("prefill32k", 4, 0), ("ep8_shard", 6, 0)])
 def test_forward_longcat_shape_sampled(name, n_sample, n_skew):
     cfg, L = layer(name)
     x = inputs.make_tokens(cfg, "cuda")
