@@ -5,6 +5,8 @@ Tolerance (max relative error per token, infinity norm): 2e-2 with bf16
 weights, 5e-2 with fp8 weights, against the fp64 oracle evaluated on the
 GPU's own selection (selection parity is checked separately, bit-exact).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -102,6 +104,32 @@ def test_forward_longcat_shape_sampled(name, n_sample, n_skew):
     print(f"{name}: mean FFN experts/token {counts[:cfg.n_ffn].sum() / cfg.tokens:.3f}, "
           f"touched {int((counts[:cfg.n_ffn] > 0).sum())}, max rows {counts[:cfg.n_ffn].max()}")
     check_rows(cfg, L, x, res, _sample(x, n_sample, n_skew))
+
+
+def test_forward_maximum_tokens():
+    # The largest batch the boundary accepts at the LongCat shape: the
+    # large-M GEMM addresses gathered x rows with 32-bit byte offsets, so
+    # T * d * 2 < 2^32 gives T = 349,525 (about 5,500 rows per FFN expert,
+    # 18 M-tiles each). The last tokens (x offsets just under 4 GiB) are
+    # checked along with the first; one token more is rejected.
+    cfg, L = layer("prefill")
+    T = (2 ** 32 - 1) // (cfg.d * 2)
+    shape = lcmoe.shape_of(cfg)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T, skew=False)
+    res = run_forward(cfg, L, x)
+    counts = res["counts"].cpu().numpy()
+    assert counts.sum() == T * cfg.k
+    print(f"T={T}: FFN slots {counts[:cfg.n_ffn].sum()}, max rows {counts[:cfg.n_ffn].max()}")
+    check_rows(cfg, L, x, res, np.array([0, 1, T // 2, T - 2, T - 1]))
+    del res
+    torch.cuda.empty_cache()
+    # T + 1 tokens: UNSUPPORTED before anything is read or enqueued
+    p = [t.data_ptr() for t in (x, L["w_router"], L["bias"], L["w13"], L["w2"])]
+    st = lcmoe.lib().lcmoe_forward(ctypes.byref(shape), T + 1, p[0], p[1], p[2], p[3], None, p[4],
+                                   None, p[0], p[0], p[0], p[0], p[0], 1 << 40, None)
+    assert st == lcmoe.ERR_UNSUPPORTED
+    del x
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 16), ("small", 1000), ("decode", 64)])
