@@ -115,7 +115,7 @@ def _sample(T, n):
     return np.array(sorted(set(np.linspace(0, T - 1, n).astype(int))))
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "prefill32k"])
 def test_backward_longcat_shape(name):
     # LongCat shape. (1) A handful of tokens on their own: every output
     # checked (dW13/dW2 on three touched experts, the rest zero). (2) The
