@@ -43,7 +43,9 @@
  *                          fp8 with d % 128 or I % 128 != 0 or d or I
  *                          above 16384, one expert's W13 of 4 GiB or
  *                          more, a tensor pointer not 16-byte aligned,
- *                          T*K >= 2^31, (forward) x of 4 GiB or more.
+ *                          T*K >= 2^31, (forward) x of 4 GiB or more,
+ *                          (backward) fp8 weights or slot rows of 4 GiB
+ *                          or more (see lcmoe_backward).
  *   LCMOE_ERR_WORKSPACE    ws is NULL or ws_bytes too small.
  *   LCMOE_ERR_HIP          a HIP launch failed (hipGetLastError).
  */
