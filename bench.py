@@ -440,9 +440,32 @@ def measure_backward(cfg, L, x, steps, warmup, hip):
     else:
         ach, peak, unit = w["flops"] / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
     flops = sum(v["flops"] for v in work.values())
-    del ws, out, dy
+    # the training pair: the forward that also stores u (fp32) and the
+    # backward that reads it instead of recomputing u = W13 x
+    u = torch.empty(lcmoe.u_rows(shape, T), 2 * cfg.inter, dtype=torch.float32, device="cuda")
+    fws = lcmoe.workspace(shape, T)
+
+    def timed(fn, n):
+        for _ in range(min(warmup, 2)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    fwd_train_ms = timed(lambda: lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"],
+                                               L["w2"], ws=fws, u_save=u), steps)
+    bwd_saved_ms = timed(lambda: lcmoe.backward(shape, x, L["w_router"], L["bias"], L["w13"],
+                                                L["w2"], dy, ws=ws, out=out, u_saved=u), steps)
+    del ws, out, dy, u, fws
     torch.cuda.empty_cache()
     return dict(tokens=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), stages_ms=stages,
+                training_pair=dict(forward_train_ms=fwd_train_ms, backward_saved_ms=bwd_saved_ms,
+                                   step_ms=fwd_train_ms + bwd_saved_ms),
                 stage_roofline=roof, dominant_kernel=dom,
                 roofline=dict(bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                               algorithmic_bytes=w["bytes"], flops=w["flops"],
@@ -573,7 +596,9 @@ def main():
             bw = res["backward"]
             print(f"[bench] {name} backward: {bw['ms_per_step']:.3f} ms/step, dominant "
                   f"{bw['dominant_kernel']} {bw['roofline']['frac']:.3f} of "
-                  f"{bw['roofline']['bound']}", file=sys.stderr, flush=True)
+                  f"{bw['roofline']['bound']}; training pair: forward with saved u "
+                  f"{bw['training_pair']['forward_train_ms']:.3f} ms + backward from it "
+                  f"{bw['training_pair']['backward_saved_ms']:.3f} ms", file=sys.stderr, flush=True)
         del keep
         torch.cuda.empty_cache()
 
@@ -603,7 +628,8 @@ def main():
         "dominant_kernel": m["dominant_kernel"],
         "cpu_baseline": baseline,
         "backward": ({k: results["prefill"]["backward"][k] for k in
-                      ("tokens", "ms_per_step", "tokens_per_s", "dominant_kernel", "roofline")}
+                      ("tokens", "ms_per_step", "tokens_per_s", "dominant_kernel", "roofline",
+                       "training_pair")}
                      if "backward" in results.get("prefill", {}) else None),
         "copy_gbps": copy_gbps,
         "detail": results,

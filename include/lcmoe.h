@@ -252,6 +252,34 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
                                    float* dw_router, void* dw13, void* dw2, void* ws,
                                    size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events);
 
+/* Training pair. lcmoe_forward_train is lcmoe_forward (bf16 weights) that
+ * also stores, for every FFN slot row, the expert pre-activations
+ * u = [W1 x; W3 x] in fp32, the accumulators its gate/up epilogue holds
+ * before the SiLU gate. lcmoe_backward_saved is lcmoe_backward taking those
+ * rows instead of recomputing u = W13 x, which saves one read of every
+ * touched expert's W13 for one write and one read of u. The routing is
+ * recomputed (same kernels, so the same selection and slot order): the
+ * backward must see the same x, router weights and bias as the forward that
+ * saved u.
+ *
+ *   u_save, u_saved  [T*min(K,N)][2I] fp32 device, written by the forward,
+ *                    read by the backward: row r is FFN slot row r of the
+ *                    layer's expert-grouped slot order (rows past the slot
+ *                    count are not touched)
+ * Other arguments as lcmoe_forward / lcmoe_backward (no fp8 scales: bf16
+ * weights only). Errors as those calls; UNSUPPORTED for fp8 weights or a
+ * misaligned u buffer, INVALID_ARG for a null u buffer with T > 0. */
+lcmoe_status lcmoe_forward_train(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                 const float* w_router, const float* bias, const void* w13,
+                                 const void* w2, void* y_bf16, int32_t* topk_idx,
+                                 float* topk_gate, int32_t* counts, void* u_save, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+lcmoe_status lcmoe_backward_saved(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                  const float* w_router, const float* bias, const void* w13,
+                                  const void* w2, const void* dy_bf16, const void* u_saved,
+                                  float* dx, float* dw_router, void* dw13, void* dw2, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* Router-side statistics ("LongCat-Flash" section 2.1, load-balance control:
  * the device-level load-balance loss L_LB = alpha * sum_{j=1..D+1} f_j P_j
  * with the zero-computation experts as group D+1; the training-stability

@@ -54,6 +54,58 @@ __global__ __launch_bounds__(256) void bwd_dg_reduce_kernel(const float* __restr
   }
 }
 
+// One wave per FFN slot row s < S (S read on the device), from the forward's
+// saved u = [a; c] (fp32) and Q_s = (W2^T dy)_s: h = silu(a) c; dg = <Q_s, h>;
+// dh = g Q_s; dU = [dh c silu'(a); dh silu(a)] and g h (bf16). Four columns
+// per lane and step.
+__global__ __launch_bounds__(256) void bwd_silu_saved_kernel(const float* __restrict__ U,
+                                                             const float* __restrict__ Q,
+                                                             const int* __restrict__ perm,
+                                                             const float* __restrict__ gate,
+                                                             const int* __restrict__ s_dev, int I,
+                                                             uint16_t* __restrict__ dU,
+                                                             uint16_t* __restrict__ Hg,
+                                                             float* __restrict__ dg) {
+  const int lane = threadIdx.x & 63;
+  const int S = *s_dev;
+  const int wpb = blockDim.x >> 6;
+  for (int s = blockIdx.x * wpb + (threadIdx.x >> 6); s < S; s += gridDim.x * wpb) {
+    const int slot = perm[s];
+    const float g = gate[slot];
+    const float* u = U + (size_t)s * 2 * I;
+    const float* q = Q + (size_t)s * I;
+    uint16_t* du = dU + (size_t)s * 2 * I;
+    uint16_t* hg = Hg + (size_t)s * I;
+    float part = 0.f;
+    for (int j = 4 * lane; j < I; j += 256) {
+      const float4 av = *reinterpret_cast<const float4*>(u + j);
+      const float4 cv = *reinterpret_cast<const float4*>(u + I + j);
+      const float4 qv = *reinterpret_cast<const float4*>(q + j);
+      const float a[4] = {av.x, av.y, av.z, av.w};
+      const float c[4] = {cv.x, cv.y, cv.z, cv.w};
+      const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+      float da[4], dc[4], h[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float sg = 1.0f / (1.0f + expf(-a[t]));
+        const float si = a[t] * sg;
+        const float hv = si * c[t];
+        part += qa[t] * hv;
+        const float dh = g * qa[t];
+        da[t] = dh * c[t] * (sg * (1.0f + a[t] * (1.0f - sg)));
+        dc[t] = dh * si;
+        h[t] = g * hv;
+      }
+      *reinterpret_cast<uint2*>(du + j) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+      *reinterpret_cast<uint2*>(du + I + j) =
+          make_uint2(pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3]));
+      *reinterpret_cast<uint2*>(hg + j) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    }
+    part = wave_sum(part);
+    if (lane == 0) dg[slot] = part;
+  }
+}
+
 // One wave per token: dg of its zero-computation slots, <dy_t, x_t>.
 __global__ __launch_bounds__(256) void bwd_zero_dg_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ dy,
@@ -210,6 +262,11 @@ void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, int* to
 void launch_bwd_dg_reduce(const float* dgp, int P, const int* perm, const int* s_dev, float* dg,
                           int grid, hipStream_t s) {
   bwd_dg_reduce_kernel<<<grid, 256, 0, s>>>(dgp, P, perm, s_dev, dg);
+}
+void launch_bwd_silu_saved(const float* U, const float* Q, const int* perm, const float* gate,
+                           const int* s_dev, int I, uint16_t* dU, uint16_t* Hg, float* dg, int grid,
+                           hipStream_t s) {
+  bwd_silu_saved_kernel<<<grid, 256, 0, s>>>(U, Q, perm, gate, s_dev, I, dU, Hg, dg);
 }
 void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, int T, int d, int K,
                         int N, float* dg, hipStream_t s) {

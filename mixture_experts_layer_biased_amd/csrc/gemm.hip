@@ -177,6 +177,13 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
             for (int v = 0; v < 4; ++v) h[v] = silu_f(acc[0][c][v]) * acc[1][c][v];
             *reinterpret_cast<uint2*>(a.out + (size_t)(row0 + r) * a.n_out + col) =
                 make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            if (!FP8 && a.usave != nullptr) {  // u = [a; c] for the backward
+              float* u = a.usave + (size_t)(row0 + r) * 2 * a.n_out;
+              *reinterpret_cast<float4*>(u + col) =
+                  make_float4(acc[0][c][0], acc[0][c][1], acc[0][c][2], acc[0][c][3]);
+              *reinterpret_cast<float4*>(u + a.n_out + col) =
+                  make_float4(acc[1][c][0], acc[1][c][1], acc[1][c][2], acc[1][c][3]);
+            }
           } else {
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
@@ -611,6 +618,25 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
   // columns: 128 bytes (down, 64 columns) or 64 bytes (gate/up, 32 columns).
   // Row r's 16-byte chunk c sits at c ^ ((r >> 1) & 7) (down, 8 chunks per
   // row) or c ^ ((r >> 2) & 3) (gate/up, 4 chunks): conflict-free both ways.
+  if (GATEUP && a.usave != nullptr) {
+    // u = [a; c] of every row for the backward: 16-byte stores, 4 columns each
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int r = frow(i) + (lane & 31);
+      if (frow(i) >= rows || r >= rows) continue;
+      float* u = a.usave + (size_t)(rowbase + r) * 2 * a.n_out;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = slice * kBigColsGateUp + 32 * wn + 8 * q + 4 * h;
+        if (j >= a.n_out) continue;
+        const f32x16_t& g = acc[i][0];
+        const f32x16_t& v = acc[i][1];
+        *reinterpret_cast<float4*>(u + j) = make_float4(g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]);
+        *reinterpret_cast<float4*>(u + a.n_out + j) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+    }
+  }
   raw_barrier();
   constexpr int CPR = GATEUP ? 4 : 8;  // 16-byte chunks per staged row
   uint4* st = lds + wave * 256;

@@ -38,6 +38,9 @@ struct GemmArgs {
   int topk;
   int n_ffn;
   int nslices;             // column blocks per expert
+  // Gate/up with bf16 weights: when not null, the pre-activations u = [a; c]
+  // of every slot row are also stored, fp32 [S][2I] in slot order.
+  float* usave;
   // Backward of gate/up (launch_gemm_big_bwd_u only): per slot row s,
   // Q = W2^T dy [S][I] fp32 and the slot gates (indexed by slot id) are read;
   // out receives g h (bf16 [S][I]), bdu dU = [dh c silu'(a); dh silu(a)]
@@ -116,6 +119,11 @@ void launch_tile_prefix(const int* counts, int N, int rows, int* prefix, int* to
 // dg of the FFN slots: dg[perm[s]] = sum over the P partials of row s, in order.
 void launch_bwd_dg_reduce(const float* dgp, int P, const int* perm, const int* s_dev, float* dg,
                           int grid, hipStream_t s);
+// The SiLU backward per FFN slot row from the forward's saved u (fp32): dU,
+// g h and dg of the slot.
+void launch_bwd_silu_saved(const float* U, const float* Q, const int* perm, const float* gate,
+                           const int* s_dev, int I, uint16_t* dU, uint16_t* Hg, float* dg, int grid,
+                           hipStream_t s);
 void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, int T, int d, int K,
                         int N, float* dg, hipStream_t s);
 void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate, const float* dg,

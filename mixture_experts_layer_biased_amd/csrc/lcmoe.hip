@@ -258,12 +258,16 @@ lcmoe_status lcmoe_permute(const lcmoe_shape* shape, int32_t T, const int32_t* t
   return hip_status();
 }
 
-lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
-                                  const float* w_router, const float* bias, const void* w13,
-                                  const float* w13_scale, const void* w2, const float* w2_scale,
-                                  void* y_bf16, int32_t* topk_idx, float* topk_gate,
-                                  int32_t* counts, void* ws, size_t ws_bytes,
-                                  hipStream_t stream, hipEvent_t* stage_events) {
+namespace {
+
+// The forward; usave (bf16 weights only, may be null) receives the gate/up
+// pre-activations of every FFN slot row.
+lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                          const float* w_router, const float* bias, const void* w13,
+                          const float* w13_scale, const void* w2, const float* w2_scale,
+                          void* y_bf16, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                          void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events,
+                          float* usave) {
   lcmoe_status st = check_shape(shape);
   if (st != LCMOE_OK) return st;
   const bool fp8 = shape->w_dtype != LCMOE_W_BF16;          // fp8 weights
@@ -351,6 +355,7 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
   a.src8 = a8 ? at<uint8_t>(base, L.xq) : nullptr;
   a.ascale = a8 ? at<float>(base, L.xs) : nullptr;
   a.out = H;
+  a.usave = usave;
   a.kdim = d;
   a.n_out = I;
   a.rows_total = 2 * I;
@@ -367,6 +372,7 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
                       stream);
 
   // down: Y = H W2^T
+  a.usave = nullptr;
   a.w = w2;
   a.wscale = w2_scale;
   a.src = H;
@@ -390,6 +396,33 @@ lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const voi
   return hip_status();
 }
 
+}  // namespace
+
+lcmoe_status lcmoe_forward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                  const float* w_router, const float* bias, const void* w13,
+                                  const float* w13_scale, const void* w2, const float* w2_scale,
+                                  void* y_bf16, int32_t* topk_idx, float* topk_gate,
+                                  int32_t* counts, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, hipEvent_t* stage_events) {
+  return forward_impl(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale, y_bf16,
+                      topk_idx, topk_gate, counts, ws, ws_bytes, stream, stage_events, nullptr);
+}
+
+lcmoe_status lcmoe_forward_train(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                 const float* w_router, const float* bias, const void* w13,
+                                 const void* w2, void* y_bf16, int32_t* topk_idx,
+                                 float* topk_gate, int32_t* counts, void* u_save, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (shape->w_dtype != LCMOE_W_BF16) return LCMOE_ERR_UNSUPPORTED;
+  if (T > 0 && u_save == nullptr) return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && !aligned16(u_save)) return LCMOE_ERR_UNSUPPORTED;
+  return forward_impl(shape, T, x_bf16, w_router, bias, w13, nullptr, w2, nullptr, y_bf16,
+                      topk_idx, topk_gate, counts, ws, ws_bytes, stream, nullptr,
+                      static_cast<float*>(u_save));
+}
+
 lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                            const float* w_router, const float* bias, const void* w13,
                            const float* w13_scale, const void* w2, const float* w2_scale,
@@ -408,11 +441,15 @@ size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_toke
   return best + kAlign;
 }
 
-lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
-                                   const float* w_router, const float* bias, const void* w13,
-                                   const void* w2, const void* dy_bf16, float* dx,
-                                   float* dw_router, void* dw13, void* dw2, void* ws,
-                                   size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+namespace {
+
+// The backward; usaved (may be null) holds the forward's gate/up
+// pre-activations, which then replace the recomputation of u.
+lcmoe_status backward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                           const float* w_router, const float* bias, const void* w13,
+                           const void* w2, const void* dy_bf16, float* dx, float* dw_router,
+                           void* dw13, void* dw2, void* ws, size_t ws_bytes, hipStream_t stream,
+                           hipEvent_t* ev, const float* usaved) {
   lcmoe_status st = check_shape(shape);
   if (st != LCMOE_OK) return st;
   if (shape->w_dtype != LCMOE_W_BF16) return LCMOE_ERR_UNSUPPORTED;
@@ -501,8 +538,11 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
 
   // 3. u = W13_e x per FFN slot row on the forward's large-M gate/up GEMM
   //    (every expert with slots, M-tiles of up to kBigTileRows rows), with the
-  //    SiLU backward in its epilogue: g h, dU and the partials of dg = <Q, h>
-  {
+  //    SiLU backward in its epilogue: g h, dU and the partials of dg = <Q, h>;
+  //    or, with the forward's saved u, the SiLU backward alone
+  if (usaved != nullptr) {
+    launch_bwd_silu_saved(usaved, Q, perm, gate, s_dev, I, dU, Hg, dg, row_grid, stream);
+  } else {
     GemmArgs ga{};
     ga.w = w13;
     ga.src = x;
@@ -530,8 +570,9 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
 
   // 4. dg of the FFN slots (sum of the partials) and of the zero slots;
   //    router dz
-  launch_bwd_dg_reduce(at<float>(base, B.dgp), 4 * B.nslices, perm, s_dev, dg,
-                       (int)std::min<long long>(4096, (smax + 255) / 256), stream);
+  if (usaved == nullptr)
+    launch_bwd_dg_reduce(at<float>(base, B.dgp), 4 * B.nslices, perm, s_dev, dg,
+                         (int)std::min<long long>(4096, (smax + 255) / 256), stream);
   launch_bwd_zero_dg(x, dy, idx, T, d, K, N, dg, stream);
   launch_bwd_router_dz(logits, idx, gate, dg, T, E, B.Ep, K, dzp, dzt, stream);
   mark(ev, 4, stream);
@@ -570,13 +611,36 @@ lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const vo
   return hip_status();
 }
 
+}  // namespace
+
+lcmoe_status lcmoe_backward_staged(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias, const void* w13,
+                                   const void* w2, const void* dy_bf16, float* dx,
+                                   float* dw_router, void* dw13, void* dw2, void* ws,
+                                   size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+  return backward_impl(shape, T, x_bf16, w_router, bias, w13, w2, dy_bf16, dx, dw_router, dw13,
+                       dw2, ws, ws_bytes, stream, ev, nullptr);
+}
+
 lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                             const float* w_router, const float* bias, const void* w13,
                             const void* w2, const void* dy_bf16, float* dx, float* dw_router,
                             void* dw13, void* dw2, void* ws, size_t ws_bytes,
                             hipStream_t stream) {
-  return lcmoe_backward_staged(shape, T, x_bf16, w_router, bias, w13, w2, dy_bf16, dx, dw_router,
-                               dw13, dw2, ws, ws_bytes, stream, nullptr);
+  return backward_impl(shape, T, x_bf16, w_router, bias, w13, w2, dy_bf16, dx, dw_router, dw13,
+                       dw2, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+lcmoe_status lcmoe_backward_saved(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                  const float* w_router, const float* bias, const void* w13,
+                                  const void* w2, const void* dy_bf16, const void* u_saved,
+                                  float* dx, float* dw_router, void* dw13, void* dw2, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (T > 0 && u_saved == nullptr) return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && !aligned16(u_saved)) return LCMOE_ERR_UNSUPPORTED;
+  return backward_impl(shape, T, x_bf16, w_router, bias, w13, w2, dy_bf16, dx, dw_router, dw13,
+                       dw2, ws, ws_bytes, stream, nullptr,
+                       static_cast<const float*>(u_saved));
 }
 
 lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all, const int32_t* counts,

@@ -19,7 +19,8 @@ W_BF16, W_FP8_E4M3_B128, W_FP8_E4M3_B128_A8 = 0, 1, 2
 EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
            "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
            "lcmoe_router_stats", "lcmoe_backward_workspace_bytes", "lcmoe_backward",
-           "lcmoe_backward_staged", "lcmoe_status_str")
+           "lcmoe_backward_staged", "lcmoe_forward_train", "lcmoe_backward_saved",
+           "lcmoe_status_str")
 NUM_STAGES = 8
 STAGES = ("router", "topk", "permute", "gateup_small", "gateup_large", "down_small",
           "down_large", "combine")
@@ -91,6 +92,10 @@ def lib():
     L.lcmoe_backward.restype = st
     L.lcmoe_backward_staged.argtypes = [S, i32] + [_P] * 11 + [sz, _P, _P]
     L.lcmoe_backward_staged.restype = st
+    L.lcmoe_forward_train.argtypes = [S, i32] + [_P] * 11 + [sz, _P]
+    L.lcmoe_forward_train.restype = st
+    L.lcmoe_backward_saved.argtypes = [S, i32] + [_P] * 12 + [sz, _P]
+    L.lcmoe_backward_saved.restype = st
     L.lcmoe_status_str.argtypes = [st]
     L.lcmoe_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -174,12 +179,20 @@ def permute(shape, topk_idx, ws=None):
     return dict(counts=counts, offsets=offsets, perm=perm, row_of_slot=row_of_slot)
 
 
+def u_rows(shape, T):
+    """Rows of the saved pre-activation buffer of a T-token call: T * min(K, N)."""
+    return int(T) * min(shape.top_k, shape.n_ffn)
+
+
 def forward(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, ws=None,
-            out=None, stage_events=None):
+            out=None, stage_events=None, u_save=None):
     """The whole layer. Returns dict(y bf16 [T,d], idx, gate, counts).
 
     stage_events: optional ctypes array of NUM_STAGES + 1 hipEvent_t handles
-    recorded at the stage boundaries (lcmoe_forward_staged)."""
+    recorded at the stage boundaries (lcmoe_forward_staged).
+    u_save: optional fp32 [u_rows(shape, T), 2I] tensor; when given, the call
+    is lcmoe_forward_train (bf16 weights), which also stores the gate/up
+    pre-activations of every FFN slot row for backward(..., u_saved=...)."""
     T, d = x.shape
     dev = x.device
     K, E = shape.top_k, shape.n_experts
@@ -191,6 +204,13 @@ def forward(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, ws
     if ws is None:
         ws = workspace(shape, T, dev)
     _dev(x, w_router, bias, w13, w2, w13_scale, w2_scale, y, idx, gate, counts, ws)
+    if u_save is not None:
+        _dev(u_save)
+        _check(lib().lcmoe_forward_train(ctypes.byref(shape), T, _ptr(x), _ptr(w_router),
+                                         _ptr(bias), _ptr(w13), _ptr(w2), _ptr(y), _ptr(idx),
+                                         _ptr(gate), _ptr(counts), _ptr(u_save), _ptr(ws),
+                                         ws.numel(), _stream()), "lcmoe_forward_train")
+        return dict(y=y, idx=idx, gate=gate, counts=counts, u=u_save)
     args = (ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13),
             _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(idx), _ptr(gate),
             _ptr(counts), _ptr(ws), ws.numel(), _stream())
@@ -244,9 +264,12 @@ def backward_workspace_bytes(shape, max_tokens):
     return int(lib().lcmoe_backward_workspace_bytes(ctypes.byref(shape), int(max_tokens)))
 
 
-def backward(shape, x, w_router, bias, w13, w2, dy, ws=None, out=None, stage_events=None):
+def backward(shape, x, w_router, bias, w13, w2, dy, ws=None, out=None, stage_events=None,
+             u_saved=None):
     """Gradients of <dy, y> for y = forward(...). Returns dict(dx fp32 [T,d],
-    dw_router fp32 [E,d], dw13 bf16 [N,2I,d], dw2 bf16 [N,d,I])."""
+    dw_router fp32 [E,d], dw13 bf16 [N,2I,d], dw2 bf16 [N,d,I]).
+    u_saved: the pre-activations a forward(..., u_save=...) stored for the
+    same x and parameters (lcmoe_backward_saved: u is not recomputed)."""
     T, d = x.shape
     dev = x.device
     E, N, I = shape.n_experts, shape.n_ffn, shape.d_expert
@@ -261,6 +284,14 @@ def backward(shape, x, w_router, bias, w13, w2, dy, ws=None, out=None, stage_eve
             raise LcmoeError(ERR_INVALID_ARG, "invalid or unsupported shape")
         ws = torch.empty(n, dtype=torch.uint8, device=dev)
     _dev(x, w_router, bias, w13, w2, dy, dx, dwr, dw13, dw2, ws)
+    if u_saved is not None:
+        _dev(u_saved)
+        _check(lib().lcmoe_backward_saved(ctypes.byref(shape), T, _ptr(x), _ptr(w_router),
+                                          _ptr(bias), _ptr(w13), _ptr(w2), _ptr(dy),
+                                          _ptr(u_saved), _ptr(dx), _ptr(dwr), _ptr(dw13),
+                                          _ptr(dw2), _ptr(ws), ws.numel(), _stream()),
+               "lcmoe_backward_saved")
+        return dict(dx=dx, dw_router=dwr, dw13=dw13, dw2=dw2)
     args = (ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13), _ptr(w2),
             _ptr(dy), _ptr(dx), _ptr(dwr), _ptr(dw13), _ptr(dw2), _ptr(ws), ws.numel(), _stream())
     if stage_events is None:

@@ -218,3 +218,23 @@ def test_backward_workspace(dims):
     S = 8192 * min(K, N)
     assert lcmoe.backward_workspace_bytes(s, 8192) >= S * (4 * d + I * 4 + d * 4 + 2 * I * 2
                                                            + I * 2)
+
+
+def test_training_pair_validation():
+    L = lcmoe.lib()
+    s = shp()
+    fwd = lambda sh, T, u: L.lcmoe_forward_train(ctypes.byref(sh), T, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                  FAKE, FAKE, FAKE, FAKE, u, None, 0, None)
+    bwd = lambda sh, T, u: L.lcmoe_backward_saved(ctypes.byref(sh), T, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                   FAKE, u, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert fwd(s, 4, None) == ERR_INVALID_ARG
+    assert fwd(s, 4, MIS) == ERR_UNSUPPORTED
+    assert fwd(s, 4, FAKE) == ERR_WORKSPACE
+    assert bwd(s, 4, None) == ERR_INVALID_ARG
+    assert bwd(s, 4, MIS) == ERR_UNSUPPORTED
+    assert bwd(s, 4, FAKE) == ERR_WORKSPACE
+    for wd in (1, 2):  # fp8 weights: no training pair
+        f = make_shape(128, 8, 4, 3, 128, wd)
+        assert fwd(f, 4, FAKE) == ERR_UNSUPPORTED
+        assert bwd(f, 4, FAKE) == ERR_UNSUPPORTED
+    assert lcmoe.u_rows(s, 10) == 10 * min(s.top_k, s.n_ffn)
