@@ -95,6 +95,22 @@ def test_backward_odd_multiples_of_32(d, inter, T):
     check_all(cfg, L, x, dy, res, gpu_selection(cfg, L, x), cache={})
 
 
+@pytest.mark.parametrize("kw,T", [
+    (dict(d=128, n_ffn=1, n_zero=0, k=1, inter=64), 100),      # one FFN expert: dz = 0
+    (dict(n_ffn=8, n_zero=4, k=12), 50),                        # K = E: a dense mixture
+    (dict(n_ffn=1536, n_zero=512, k=64, inter=32), 64),          # the largest E and K accepted
+])
+def test_backward_degenerate_shapes(kw, T):
+    cfg, L = layer("tiny", **kw)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=T)
+    res = run_backward(cfg, L, x, dy)
+    check_all(cfg, L, x, dy, res, gpu_selection(cfg, L, x), cache={})
+    if cfg.n_ffn == 1 and cfg.n_zero == 0:
+        # one expert: the softmax is constant, so the router gets no gradient
+        assert float(res["dw_router"].abs().max()) == 0.0
+
+
 def test_backward_zero_routing_closed_form():
     # FFN experts biased out: y_t = (sum_k g_tk) x_t, so
     # dx_t = G_t dy_t + W_r^T dz_t and every expert weight gradient is zero.

@@ -83,6 +83,22 @@ def test_forward_k_odd_multiple_of_32(d, inter, T):
     check_rows(cfg, L, x, res, np.arange(T), cache={})
 
 
+@pytest.mark.parametrize("kw,T", [
+    (dict(d=128, n_ffn=1, n_zero=0, k=1, inter=64), 100),      # one FFN expert: g = 1, y = FFN(x)
+    (dict(n_ffn=8, n_zero=4, k=12), 50),                        # K = E: a dense mixture
+    (dict(n_ffn=1536, n_zero=512, k=64, inter=32), 64),          # the largest E and K accepted
+    (dict(n_ffn=2, n_zero=2040, k=2), 200),                      # almost only zero experts
+])
+def test_forward_degenerate_shapes(kw, T):
+    cfg, L = layer("tiny", **kw)
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    res = run_forward(cfg, L, x)
+    check_routing_consistent(cfg, L, x, res)
+    check_rows(cfg, L, x, res, np.arange(T), cache={})
+    if cfg.n_ffn == 1 and cfg.n_zero == 0:
+        assert np.all(res["gate"].cpu().numpy() == 1.0)
+
+
 def _sample(x, n, extra_large=0):
     T = x.shape[0]
     toks = list(np.linspace(0, T - 1, n).astype(int))
