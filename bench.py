@@ -494,6 +494,49 @@ def copy_bandwidth(nbytes=4 << 30, reps=5):
     return gbps
 
 
+def vendor_gemm(cfg, counts, stages, reps=5):
+    """The vendor library's dense batched product (torch.bmm, i.e. hipBLASLt)
+    at the large-path shape of the layer, next to the grouped kernels' own
+    figures: every expert of the large path (more than 32 routed rows) gets
+    the mean row count of those experts, rounded up to 32; bf16 operands
+    [batch][k][n] with a contiguous right operand; fp32 accumulation.
+    Context only: a dense product, with no row gather, no ragged row counts
+    and no SiLU epilogue. bf16 weights only."""
+    import torch
+    rows = counts[: cfg.n_ffn]
+    big = rows[rows > 32]
+    if cfg.wdtype != "bf16" or big.size == 0:
+        return None
+    nb = int(big.size)
+    m = int(-(-int(np.ceil(big.mean())) // 32) * 32)
+    work = kernel_work(cfg, counts)
+    out = {"experts": nb, "rows_per_expert": m}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, k, n in (("gateup", cfg.d, 2 * cfg.inter), ("down", cfg.inter, cfg.d)):
+        a = torch.randn(nb, m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(nb, k, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        c = torch.bmm(a, b)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.bmm(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 2.0 * nb * m * k * n
+        own = work[f"{name}_large"]
+        own_ms = stages[f"{name}_large"]
+        out[name] = dict(vendor_ms=ms, vendor_tflops=flops / ms / 1e9,
+                         vendor_frac=flops / (ms / 1e3) / PEAK_BF16,
+                         grouped_ms=own_ms, grouped_tflops=own["flops"] / own_ms / 1e9,
+                         grouped_frac=own["flops"] / (own_ms / 1e3) / PEAK_BF16)
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, L, x, out, n_experts_sample):
     """The oracle on a bounded sample of the same workload: the full router,
     selection and gates for all T tokens, plus the SiLU-gated FFN of a sample
@@ -544,6 +587,9 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="measure only the backward on the prefill batch (for profiling runs)")
     ap.add_argument("--cpu-experts", type=int, default=160)
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor library's dense batched product at the large-path "
+                         "shape of each bf16 workload (context, not part of the layer)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="fold rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
@@ -584,6 +630,14 @@ def main():
         cfg = inputs.CONFIGS[name]
         res, keep = measure(cfg, args.steps, args.warmup, hip)
         results[name] = res
+        if args.vendor_gemm:
+            res["vendor_gemm"] = vendor_gemm(cfg, keep[2]["counts"].cpu().numpy(), res["stages_ms"])
+            if res["vendor_gemm"]:
+                vg = res["vendor_gemm"]
+                print(f"[bench] {name} vendor dense bmm ({vg['experts']} x {vg['rows_per_expert']} "
+                      f"rows): gate/up {vg['gateup']['vendor_tflops']:.0f} TFLOP/s vs grouped "
+                      f"{vg['gateup']['grouped_tflops']:.0f}; down {vg['down']['vendor_tflops']:.0f} "
+                      f"vs {vg['down']['grouped_tflops']:.0f}", file=sys.stderr, flush=True)
         print(f"[bench] {name}: {res['ms_per_step']:.3f} ms/step, "
               f"{res['tokens_per_s']:.0f} tok/s, dominant {res['dominant_kernel']} "
               f"{res['roofline']['frac']:.3f} of {res['roofline']['bound']}; router stats "
