@@ -12,11 +12,12 @@
 //    into MFMA A-operand registers (v_mfma_f32_16x16x32_bf16, weights as the
 //    16-row side, tokens as the 16-column side staged in LDS). Weight bytes
 //    dominate; every weight of a touched expert is read once.
-//  * large-M (33+ rows, prefill batches): 256 token rows x 256 weight rows
-//    per block, 8 waves (2 x 4), v_mfma_f32_32x32x16_bf16, both operands
-//    copied HBM -> LDS by global_load_lds_dwordx4 in a multi-stage ring; the
-//    tiles of one expert (column slices, M-tiles) are adjacent on one XCD
-//    (blockIdx % 8) so its gathered x rows are shared through that XCD's L2.
+//  * large-M (33+ rows, prefill batches): M-tiles of up to 320 token rows
+//    (kBigTileRows) x 256 weight rows per block, 8 waves (2 x 4),
+//    v_mfma_f32_32x32x16_bf16, both operands copied HBM -> LDS by
+//    global_load_lds_dwordx4 in a multi-stage ring; the tiles of one expert
+//    (column slices, M-tiles) are adjacent on one XCD (blockIdx % 8) so its
+//    gathered x rows are shared through that XCD's L2.
 // fp8 (E4M3FN, one fp32 scale per 128x128 block) weights are converted in
 // registers: bf16(fl32(q) * s), then the same bf16 MFMA.
 #include <type_traits>
