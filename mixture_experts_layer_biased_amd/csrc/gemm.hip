@@ -33,9 +33,12 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 // small-M kernel
 // ===========================================================================
 constexpr int kSmallLdsChunks = 4096;  // 64 KB of staged token rows
-// Token rows are staged with a pitch of 128 or 256 chunks (a multiple of
-// the 256-byte bank window), chunk c of row r at c ^ (r & 15): the 16 rows
-// one MFMA operand read touches at the same chunk hit 16 distinct slots.
+// Token rows are staged with a pitch of 128, 256 or 1024 chunks (a multiple
+// of the 256-byte bank window), chunk c of row r at c ^ (r & 15): the 16
+// rows one MFMA operand read touches at the same chunk hit 16 distinct
+// slots. With up to 4 routed rows only 4 rows are staged (so one fill holds
+// 8192 k: all of k at the layer's shapes), and operand reads of rows 4..15,
+// whose results are never stored, read row 0.
 
 template <bool GATEUP, bool FP8>
 __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
@@ -51,8 +54,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
     const int rows = a.counts[e];
     const int row0 = a.offsets[e];
     const int ncb = rows <= 16 ? 1 : 2;
-    const int kc = (kSmallLdsChunks * 8) / (16 * ncb);  // k elements per LDS fill
-    const int cpr = kc >> 3;                              // LDS row pitch (chunks)
+    const int rcap = rows <= 4 ? 4 : 16 * ncb;      // staged rows
+    const int kc = (kSmallLdsChunks * 8) / rcap;    // k elements per LDS fill
+    const int cpr = kc >> 3;                        // LDS row pitch (chunks)
 
     // Two 16-row weight fragments per wave.
     int fbase0, fbase1, ocol0;
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (c < ncb) {
-            const int r = 16 * c + lr;
+            const int r = 16 * c + lr < rcap ? 16 * c + lr : 0;
             const bf16x8_t B = as_bf16x8(sX[r * cpr + (ch ^ (r & 15))]);
             acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[0][c], 0, 0, 0);
             acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[1][c], 0, 0, 0);
@@ -137,9 +141,17 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
       }
     };
 
+    uint4 w0[2][4], w1[2][4];
     for (int kc0 = 0; kc0 < kdim; kc0 += kc) {
       const int kcl = min(kc, kdim - kc0);
       const int ccl = kcl >> 3;
+      const int kend = kc0 + kcl;
+      // The fill's first two weight steps are requested before its token
+      // rows are staged, so the weight stream runs on through the staging.
+      if (active) {
+        load_w(w0, kc0);
+        if (kc0 + 128 < kend) load_w(w1, kc0 + 128);
+      }
       __syncthreads();  // previous LDS fill fully consumed
       for (int id = tid; id < rows * ccl; id += 256) {
         const int r = id / ccl, c = id - r * ccl;
@@ -152,15 +164,12 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
       }
       __syncthreads();
       if (active) {
-        const int kend = kc0 + kcl;
-        uint4 w0[2][4], w1[2][4];
-        load_w(w0, kc0);
         for (int kb = kc0; kb < kend; kb += 256) {
-          if (kb + 128 < kend) load_w(w1, kb + 128);
           compute(w0, kb, kc0);
+          if (kb + 256 < kend) load_w(w0, kb + 256);
           if (kb + 128 < kend) {
-            if (kb + 256 < kend) load_w(w0, kb + 256);
             compute(w1, kb + 128, kc0);
+            if (kb + 384 < kend) load_w(w1, kb + 384);
           }
         }
       }
