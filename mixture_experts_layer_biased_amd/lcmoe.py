@@ -125,6 +125,39 @@ def _dev(*ts):
             assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA tensors"
 
 
+def _expect(name, t, dtype, shape):
+    """The library reads and writes through raw pointers with the sizes the
+    shape implies, so every tensor's dtype and shape are checked here first."""
+    if t is None or t.dtype != dtype or tuple(t.shape) != tuple(int(v) for v in shape):
+        got = "None" if t is None else f"{t.dtype} {tuple(t.shape)}"
+        raise LcmoeError(ERR_INVALID_ARG,
+                         f"{name}: expected {dtype} {tuple(int(v) for v in shape)}, got {got}")
+
+
+def _expect_layer(shape, T, x, w_router, bias):
+    d, E = shape.d_model, shape.n_experts
+    _expect("x", x, torch.bfloat16, (T, d))
+    _expect("w_router", w_router, torch.float32, (E, d))
+    _expect("bias", bias, torch.float32, (E,))
+
+
+def _expect_experts(shape, w13, w2, w13_scale=None, w2_scale=None):
+    d, N, I = shape.d_model, shape.n_ffn, shape.d_expert
+    wdt = torch.bfloat16 if shape.w_dtype == W_BF16 else torch.uint8
+    _expect("w13", w13, wdt, (N, 2 * I, d))
+    _expect("w2", w2, wdt, (N, d, I))
+    if shape.w_dtype != W_BF16:
+        _expect("w13_scale", w13_scale, torch.float32, (N, 2 * I // 128, d // 128))
+        _expect("w2_scale", w2_scale, torch.float32, (N, d // 128, I // 128))
+
+
+def _expect_routing_out(shape, T, idx, gate, counts):
+    K, E = shape.top_k, shape.n_experts
+    _expect("idx", idx, torch.int32, (T, K))
+    _expect("gate", gate, torch.float32, (T, K))
+    _expect("counts", counts, torch.int32, (E,))
+
+
 def workspace_bytes(shape, max_tokens):
     return int(lib().lcmoe_workspace_bytes(ctypes.byref(shape), int(max_tokens)))
 
@@ -144,10 +177,12 @@ def route(shape, x, w_router, bias, ws=None, logits=False, out=None):
     T = x.shape[0]
     dev = x.device
     K, E = shape.top_k, shape.n_experts
+    _expect_layer(shape, T, x, w_router, bias)
     o = out or {}
     idx = o.get("idx", torch.empty(T, K, dtype=torch.int32, device=dev))
     gate = o.get("gate", torch.empty(T, K, dtype=torch.float32, device=dev))
     counts = o.get("counts", torch.empty(E, dtype=torch.int32, device=dev))
+    _expect_routing_out(shape, T, idx, gate, counts)
     lg = torch.empty(T, E, dtype=torch.float32, device=dev) if logits else None
     if ws is None:
         ws = workspace(shape, T, dev)
@@ -166,6 +201,7 @@ def permute(shape, topk_idx, ws=None):
     T = topk_idx.shape[0]
     dev = topk_idx.device
     K, E, N = shape.top_k, shape.n_experts, shape.n_ffn
+    _expect("topk_idx", topk_idx, torch.int32, (T, K))
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(N + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * K, dtype=torch.int32, device=dev)
@@ -193,14 +229,20 @@ def forward(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, ws
     u_save: optional fp32 [u_rows(shape, T), 2I] tensor; when given, the call
     is lcmoe_forward_train (bf16 weights), which also stores the gate/up
     pre-activations of every FFN slot row for backward(..., u_saved=...)."""
-    T, d = x.shape
+    T = x.shape[0]
     dev = x.device
-    K, E = shape.top_k, shape.n_experts
+    K, E, d = shape.top_k, shape.n_experts, shape.d_model
+    _expect_layer(shape, T, x, w_router, bias)
+    _expect_experts(shape, w13, w2, w13_scale, w2_scale)
     o = out or {}
     y = o.get("y", torch.empty(T, d, dtype=torch.bfloat16, device=dev))
     idx = o.get("idx", torch.empty(T, K, dtype=torch.int32, device=dev))
     gate = o.get("gate", torch.empty(T, K, dtype=torch.float32, device=dev))
     counts = o.get("counts", torch.empty(E, dtype=torch.int32, device=dev))
+    _expect("y", y, torch.bfloat16, (T, d))
+    _expect_routing_out(shape, T, idx, gate, counts)
+    if u_save is not None:
+        _expect("u_save", u_save, torch.float32, (u_rows(shape, T), 2 * shape.d_expert))
     if ws is None:
         ws = workspace(shape, T, dev)
     _dev(x, w_router, bias, w13, w2, w13_scale, w2_scale, y, idx, gate, counts, ws)
@@ -223,6 +265,8 @@ def forward(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, ws
 
 def bias_update(shape, counts, mu, k_e, bias, t_all):
     """In-place bias update of the N FFN experts from `counts` of a T_all-token batch."""
+    _expect("counts", counts, torch.int32, (shape.n_experts,))
+    _expect("bias", bias, torch.float32, (shape.n_experts,))
     _dev(counts, bias)
     _check(lib().lcmoe_bias_update(ctypes.byref(shape), int(t_all), _ptr(counts),
                                    float(mu), float(k_e), _ptr(bias), _stream()),
@@ -241,6 +285,9 @@ def router_stats(shape, x, logits, counts, n_groups, k_e, alpha=1.0, lam=1.0, ws
     [2 + 2(D+1)]: L_LB, L_Z, f_1..f_{D+1}, P_1..P_{D+1}."""
     T = x.shape[0]
     dev = x.device
+    _expect("x", x, torch.bfloat16, (T, shape.d_model))
+    _expect("logits", logits, torch.float32, (T, shape.n_experts))
+    _expect("counts", counts, torch.int32, (shape.n_experts,))
     stats = torch.empty(2 + 2 * (int(n_groups) + 1), dtype=torch.float64, device=dev)
     if ws is None:
         n = router_stats_workspace_bytes(shape, n_groups)
@@ -270,14 +317,23 @@ def backward(shape, x, w_router, bias, w13, w2, dy, ws=None, out=None, stage_eve
     dw_router fp32 [E,d], dw13 bf16 [N,2I,d], dw2 bf16 [N,d,I]).
     u_saved: the pre-activations a forward(..., u_save=...) stored for the
     same x and parameters (lcmoe_backward_saved: u is not recomputed)."""
-    T, d = x.shape
+    T = x.shape[0]
     dev = x.device
-    E, N, I = shape.n_experts, shape.n_ffn, shape.d_expert
+    E, N, I, d = shape.n_experts, shape.n_ffn, shape.d_expert, shape.d_model
+    _expect_layer(shape, T, x, w_router, bias)
+    _expect_experts(shape, w13, w2)
+    _expect("dy", dy, torch.bfloat16, (T, d))
     o = out or {}
     dx = o.get("dx", torch.empty(T, d, dtype=torch.float32, device=dev))
     dwr = o.get("dw_router", torch.empty(E, d, dtype=torch.float32, device=dev))
     dw13 = o.get("dw13", torch.empty(N, 2 * I, d, dtype=torch.bfloat16, device=dev))
     dw2 = o.get("dw2", torch.empty(N, d, I, dtype=torch.bfloat16, device=dev))
+    _expect("dx", dx, torch.float32, (T, d))
+    _expect("dw_router", dwr, torch.float32, (E, d))
+    _expect("dw13", dw13, torch.bfloat16, (N, 2 * I, d))
+    _expect("dw2", dw2, torch.bfloat16, (N, d, I))
+    if u_saved is not None:
+        _expect("u_saved", u_saved, torch.float32, (u_rows(shape, T), 2 * I))
     if ws is None:
         n = backward_workspace_bytes(shape, T)
         if n == 0:
