@@ -359,6 +359,74 @@ def measure(cfg, steps, warmup, hip):
     return res, (L, x, out)
 
 
+def measure_small(steps, warmup):
+    """The small bf16 layer (d=1024, 64 FFN + 32 zero experts, K=6, I=512,
+    T=4096): its 201 MB of expert weights fit in the 256 MB MALL, so each
+    call is timed warm (weights may stay in the MALL between calls) and cold
+    (a 1 GiB scratch buffer written between calls, outside the timed region),
+    and warm once more as a replayed HIP graph of the same call (this layer is
+    small enough for the launch gaps between its kernels to show). Median per
+    call, tokens/s, and the fraction of the HBM roof from the layer's
+    algorithmic bytes."""
+    import torch
+    from mixture_experts_layer_biased_amd import inputs, lcmoe
+
+    cfg = inputs.CONFIGS["small"]
+    L = inputs.make_layer(cfg, "cuda")
+    x = inputs.make_tokens(cfg, "cuda")
+    shape = lcmoe.shape_of(cfg)
+    T = cfg.tokens
+    ws = lcmoe.workspace(shape, T)
+    out = dict(y=torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"),
+               idx=torch.empty(T, cfg.k, dtype=torch.int32, device="cuda"),
+               gate=torch.empty(T, cfg.k, dtype=torch.float32, device="cuda"),
+               counts=torch.empty(cfg.n_experts, dtype=torch.int32, device="cuda"))
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def call():
+        lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"], ws=ws, out=out)
+
+    # The same call captured once into a HIP graph (the forward enqueues
+    # kernels only), replayed warm: the launch gaps between its kernels go.
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("warm", "cold", "graph"):
+        for _ in range(warmup):
+            graph.replay() if mode == "graph" else call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            if mode == "cold":
+                scratch.fill_(i & 255)
+            a.record()
+            if mode == "graph":
+                graph.replay()
+            else:
+                call()
+            b.record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        res[mode] = dict(ms_median=float(np.median(ms)), ms_min=float(ms.min()),
+                         tokens_per_s=T / (float(np.median(ms)) / 1e3))
+    counts = out["counts"].cpu().numpy()
+    lb = layer_bytes(cfg, counts, T)
+    for mode in res:
+        res[mode]["hbm_frac"] = lb / (res[mode]["ms_median"] / 1e3) / PEAK_HBM
+    res.update(tokens=T, algorithmic_bytes=lb,
+               touched_experts=int((counts[: cfg.n_ffn] > 0).sum()),
+               config=(f"T={T}, d_model={cfg.d}, {cfg.n_ffn} FFN + {cfg.n_zero} zero experts, "
+                       f"K={cfg.k}, I={cfg.inter}, bf16, router bias ~ N(0, {cfg.bias_std})"))
+    del L, x, ws, out, scratch, graph
+    torch.cuda.empty_cache()
+    return res
+
+
 def backward_work(cfg, counts, T):
     """Algorithmic bytes and flops of each backward stage (bf16 operands,
     fp32 slot-row intermediates): per FFN slot the operand rows are read once
@@ -655,6 +723,13 @@ def main():
                   f"{bw['training_pair']['backward_saved_ms']:.3f} ms", file=sys.stderr, flush=True)
         del keep
         torch.cuda.empty_cache()
+
+    if not args.only:
+        sm = measure_small(args.steps, args.warmup)
+        results["small"] = sm
+        print(f"[bench] small (d=1024, T=4096): warm {sm['warm']['ms_median']:.3f} ms, cold "
+              f"{sm['cold']['ms_median']:.3f} ms ({sm['cold']['hbm_frac']:.3f} of HBM), graph "
+              f"replay {sm['graph']['ms_median']:.3f} ms", file=sys.stderr, flush=True)
 
     main_name = names[0]
     m = results[main_name]
