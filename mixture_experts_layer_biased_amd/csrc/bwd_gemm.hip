@@ -397,6 +397,218 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
     }
 }
 
+// Weight-gradient GEMMs (bf16 outputs dW2, dW13), persistent: one block per
+// CU walks a run of its XCD's tiles (positions pos, pos + P, ... of the XCD's
+// contiguous run, so the tiles running at once on an XCD stay adjacent), and
+// the k stages of its consecutive tiles form one stream through the
+// two-slot ring. At a prefill batch K (an expert's slot count) is about 128,
+// two stages: a tile of its own would wait for its first loads, multiply
+// for two stages and store; in the stream, the next tile's first stage
+// loads while the current tile finishes and stores. A tile's epilogue
+// stages through the slot its last stage has just released. Every wait
+// drains all of this wave's outstanding memory operations (copies and the
+// previous epilogue's stores alike). Tiles of experts without slots (zero
+// gradient) are written with plain stores, outside the stream.
+template <int WM, int WN, int FM, int FN, int OP>
+__global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmArgs g) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per stage
+  constexpr int SLOT = A_CH + B_CH;
+  constexpr int NB = SLOT / 64;                // 1 KB copy blocks per stage
+  constexpr int CPW = NB / NW;                 // copies per wave per stage
+  constexpr int JA = (A_CH / 64) / NW;         // the first JA of them fill A
+  static_assert(FM % 2 == 0 && FN % 2 == 0, "stores go by 64 x 64 sub-tiles");
+  static_assert(NB % NW == 0 && (A_CH / 64) % NW == 0, "copy blocks must split evenly");
+  static_assert(NW * 512 <= SLOT, "the epilogue stages through one slot");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "i-contiguous tiles are 128 wide");
+  constexpr int MAX_N = 2048;  // FFN experts (the shape check caps E at 2048)
+  __shared__ uint4 lds[2 * SLOT];
+  // Every expert's slot count and first slot, read once: a tile's setup
+  // then costs LDS reads instead of two dependent global loads.
+  __shared__ int s_cnt[MAX_N], s_off[MAX_N];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int h = lane >> 5, lr = lane & 31;
+
+  const int ntn = (g.N + BN - 1) / BN, mtn = (g.M + BM - 1) / BM;
+  const int total = g.n_ffn * mtn * ntn;
+  const int per_xcd = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7, pstep = gridDim.x >> 3;
+  const int rlim = min(g.M, g.m_store);  // output rows stored
+
+  struct Tile {
+    bool valid;
+    int e, m0, n0, K, nst;
+    const char* abase;
+    const char* bbase;
+  };
+  auto tile_at = [&](int pos) {
+    Tile t{};
+    const int L = xcd * per_xcd + pos;
+    t.valid = pos < per_xcd && L < total;
+    if (!t.valid) return t;
+    t.e = L / (mtn * ntn);
+    const int local = L - t.e * mtn * ntn;
+    const int mt = local / ntn;
+    t.m0 = mt * BM;
+    t.n0 = (local - mt * ntn) * BN;
+    t.K = s_cnt[t.e];
+    t.nst = (t.K + BK - 1) / BK;
+    const int off_e = s_off[t.e];
+    t.abase = reinterpret_cast<const char*>(g.a) + (size_t)off_e * g.a_ld * 2;
+    t.bbase = reinterpret_cast<const char*>(g.b) + (size_t)off_e * g.b_ld * 2;
+    return t;
+  };
+  // A tile of an expert without slots: zeros, written directly.
+  auto store_zero_tile = [&](const Tile& t) {
+    for (int id = tid; id < BM * (BN / 8); id += NT) {
+      const int r = t.m0 + id / (BN / 8), c = t.n0 + 8 * (id % (BN / 8));
+      if (r < rlim && c < g.N)
+        *reinterpret_cast<uint4*>(static_cast<char*>(g.c) +
+                                  (((long long)t.e * g.M + r) * g.c_ld + c) * 2) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // Position of the first tile at or after pos with slots (zero-filling the
+  // tiles before it when asked), or an invalid position.
+  auto next_with_slots = [&](int pos, bool zero_fill) {
+    for (;; pos += pstep) {
+      const Tile t = tile_at(pos);
+      if (!t.valid || t.nst > 0) return pos;
+      if (zero_fill) store_zero_tile(t);
+    }
+  };
+
+  // Per-lane copy descriptors (tile independent): copy j of this wave fills
+  // 1 KB block wave + NW j of the stage (A blocks first, then B); both
+  // operands are i-contiguous [64 k][128 i] sub-tiles: sub-tile b / 16, k
+  // rows 4 (b % 16) + lane / 16, swizzled 64-byte window of the lane.
+  int ccol[CPW], krow[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int b = j < JA ? wave + NW * j : wave + NW * j - A_CH / 64;
+    const int q = b >> 4, bb = b & 15;
+    const int k = 4 * bb + (lane >> 4), pc = lane & 15;
+    const int c = ((((pc >> 2) ^ (k & 3))) << 2) | (pc & 3);
+    ccol[j] = 128 * q + 8 * c;
+    krow[j] = k;
+  }
+  auto issue = [&](const Tile& t, int s, int slot) {
+    const int k0 = s * BK;
+    const int kmax = t.K - 1 - k0;  // rows past K re-load row K - 1
+    uint4* dst = lds + slot * SLOT;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const bool isA = j < JA;
+      const long long ld = isA ? g.a_ld : g.b_ld;
+      const int ext = isA ? g.M : g.N;
+      int col = (isA ? t.m0 : t.n0) + ccol[j];
+      if (col > ext - 8) col = ext - 8;
+      const int k = krow[j] < kmax ? krow[j] : kmax;
+      bdma16((isA ? t.abase : t.bbase) + (size_t)k0 * ld * 2,
+             (uint32_t)(col * 2) + (uint32_t)(k * ld * 2), dst + 64 * (wave + NW * j));
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+  auto compute = [&](const Tile& t, int s, int slot) {
+    const uint4* A = lds + slot * SLOT;
+    const uint4* B = A + A_CH;
+    const int krem = t.K - s * BK;  // valid k in this stage
+    const int nkk = min(4, (krem + 15) >> 4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk >= nkk) break;
+      bf16x8_t av[FM], bv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = 32 * FM * wm + 32 * i;
+        av[i] = km_frag(A + (r >> 7) * 1024, r & 127, kk, lane);
+      }
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int r = 32 * FN * wn + 32 * f;
+        bv[f] = km_frag(B + (r >> 7) * 1024, r & 127, kk, lane);
+      }
+      if (16 * kk + 16 > krem) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) av[i] = mask_k(av[i], kk, h, krem);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) bv[f] = mask_k(bv[f], kk, h, krem);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[f], av[i], acc[i][f], 0, 0, 0);
+    }
+  };
+
+  for (int j = tid; j < g.n_ffn; j += NT) {
+    s_cnt[j] = g.counts[j];
+    s_off[j] = g.offsets[j];
+  }
+  __syncthreads();
+  int cur_pos = next_with_slots((int)(blockIdx.x >> 3), true);
+  Tile cur = tile_at(cur_pos);
+  if (!cur.valid) return;  // block-uniform
+  // The stream: stage number n of the block goes into slot n & 1; `la` is
+  // the next stage to issue (tile la_t at la_pos, stage la_s).
+  int la_pos = cur_pos, la_s = 0;
+  Tile la_t = cur;
+  int issued = 0;
+  auto issue_next = [&]() {
+    if (!la_t.valid) return;
+    issue(la_t, la_s, issued & 1);
+    ++issued;
+    if (++la_s >= la_t.nst) {
+      la_pos = next_with_slots(la_pos + pstep, true);
+      la_t = tile_at(la_pos);
+      la_s = 0;
+    }
+  };
+  bwait_vmcnt<0>();  // the loads of the tile setup have landed
+  issue_next();      // stage 0
+  int n = 0;         // stream stage being multiplied
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
+    for (int s = 0; s < cur.nst; ++s, ++n) {
+      // Stage n has landed (and anything older, a previous epilogue's stores
+      // included); the barrier publishes it and frees slot (n + 1) & 1, which
+      // held stage n - 1 or the previous tile's epilogue staging.
+      bwait_vmcnt<0>();
+      braw_barrier();
+      issue_next();  // stage n + 1
+      compute(cur, s, n & 1);
+    }
+    // Epilogue through the slot of the stage just multiplied (stage n - 1)
+    // once every wave is done with it; stage n may be loading into the other.
+    braw_barrier();
+    uint4* st = lds + ((n - 1) & 1) * SLOT + wave * 512;
+#pragma unroll
+    for (int i2 = 0; i2 < FM / 2; ++i2)
+#pragma unroll
+      for (int f2 = 0; f2 < FN / 2; ++f2) {
+        const int r0 = cur.m0 + 32 * FM * wm + 64 * i2, c0 = cur.n0 + 32 * FN * wn + 64 * f2;
+        char* obase = static_cast<char*>(g.c) + (((long long)cur.e * g.M + r0) * g.c_ld + c0) * 2;
+        const f32x16_t sub[2][2] = {{acc[2 * i2][2 * f2], acc[2 * i2][2 * f2 + 1]},
+                                    {acc[2 * i2 + 1][2 * f2], acc[2 * i2 + 1][2 * f2 + 1]}};
+        store_subtile<false>(sub, st, lane, obase, g.c_ld, rlim - r0, g.N - c0);
+      }
+    cur_pos = next_with_slots(cur_pos + pstep, false);
+    cur = tile_at(cur_pos);
+    if (!cur.valid) break;  // block-uniform; nothing is left in flight but stores
+  }
+}
+
 // One wave per FFN slot row s < S (S read on the device): the token's x and
 // dy rows copied into slot order.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
@@ -427,10 +639,22 @@ int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols) {
   const long long items = (smax / kBwdTileM + n_ffn) * ((n_cols + kBwdTileNDgrad - 1) / kBwdTileNDgrad);
   return (int)std::min<long long>(items + 8, 1ll << 30);
 }
+// Grid of the persistent weight-gradient launch: one block per CU (its LDS
+// ring takes most of a CU's 160 KB), a multiple of 8 for the per-XCD
+// layout, and no more blocks than tiles allow.
 int bwd_wgrad_grid(int n_ffn, int M, int N) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
   const long long items = (long long)n_ffn * ((M + kWgradBM - 1) / kWgradBM) *
                           ((N + kWgradBN - 1) / kWgradBN);
-  return (int)std::min<long long>(items + 8, 1ll << 30);
+  const long long blocks = std::min<long long>((cus + 7) / 8 * 8, (items + 7) / 8 * 8);
+  return (int)std::max<long long>(8, blocks);
 }
 
 void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
@@ -445,11 +669,9 @@ void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
 }
 void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
   if (op == kBwdDw2)
-    bwd_gemm_kernel<true, true, false, kWgWM, kWgWN, kWgFM, kWgFN, 2, kBwdDw2>
-        <<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
+    bwd_wgrad_stream_kernel<kWgWM, kWgWN, kWgFM, kWgFN, kBwdDw2><<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
   else
-    bwd_gemm_kernel<true, true, false, kWgWM, kWgWN, kWgFM, kWgFN, 2, kBwdDw13>
-        <<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
+    bwd_wgrad_stream_kernel<kWgWM, kWgWN, kWgFM, kWgFN, kBwdDw13><<<grid, 64 * kWgWM * kWgWN, 0, s>>>(g);
 }
 void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s) {
   const long long items = (long long)g.n_ffn * ((g.M + 127) / 128) * ((g.N + 127) / 128);
