@@ -88,9 +88,10 @@ def bwd_stage_of_kernel(name):
     """Map a kernel symbol of a backward-only run to its backward stage."""
     if "gemm_big_dma_kernel<true, false, true>" in name:
         return "u_silu"
-    if "bwd_gemm_kernel<" in name:
-        op = int(name.split("bwd_gemm_kernel<")[1].split(">")[0].split(",")[-1])
-        return BWD_OPS.get(op)
+    for kname in ("bwd_gemm_kernel<", "bwd_wgrad_stream_kernel<"):
+        if kname in name:
+            op = int(name.split(kname)[1].split(">")[0].split(",")[-1])
+            return BWD_OPS.get(op)
     for key, stage in (("gather_rows", "route_gather"), ("router_gemm", "route_gather"),
                        ("topk", "route_gather"), ("hist_kernel", "route_gather"),
                        ("colscan", "route_gather"), ("schedule_kernel", "route_gather"),

@@ -69,6 +69,10 @@ def test_stage_maps():
         "void lcmoe::bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, 3>(lcmoe::BwdGemmArgs)") \
         == "dx_rows"
     assert bench.bwd_stage_of_kernel(
+        "void lcmoe::bwd_wgrad_stream_kernel<2, 4, 4, 2, 5>(lcmoe::BwdGemmArgs)") == "dw13"
+    assert bench.bwd_stage_of_kernel(
+        "void lcmoe::bwd_wgrad_stream_kernel<2, 4, 4, 2, 4>(lcmoe::BwdGemmArgs)") == "dw2"
+    assert bench.bwd_stage_of_kernel(
         "void lcmoe::gemm_big_dma_kernel<true, false, true>(lcmoe::GemmArgs)") == "u_silu"
     assert bench.bwd_stage_of_kernel("lcmoe::gather_rows_kernel(unsigned short const*)") \
         == "route_gather"
