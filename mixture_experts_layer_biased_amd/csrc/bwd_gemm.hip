@@ -134,13 +134,18 @@ __device__ __forceinline__ bf16x8_t km_frag(const uint4* sub, int base, int kk, 
 }
 
 // Zero the operand elements whose k (16 kk + 8 h + t within the stage) is at
-// or past krem.
+// or past krem, a dword (two elements) at a time.
 __device__ __forceinline__ bf16x8_t mask_k(bf16x8_t v, int kk, int h, int krem) {
-  const int k0 = 16 * kk + 8 * h;
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    if (k0 + t >= krem) v[t] = 0;
-  return v;
+  const int nv = krem - (16 * kk + 8 * h);  // valid elements among the lane's 8
+  uint4 u = *reinterpret_cast<uint4*>(&v);
+  auto keep = [&](int j) {  // dword j holds elements 2 j (low half) and 2 j + 1
+    return nv >= 2 * j + 2 ? 0xffffffffu : (nv == 2 * j + 1 ? 0x0000ffffu : 0u);
+  };
+  u.x &= keep(0);
+  u.y &= keep(1);
+  u.z &= keep(2);
+  u.w &= keep(3);
+  return *reinterpret_cast<bf16x8_t*>(&u);
 }
 
 // Store one wave's 64 x 64 output sub-tile (the transposed-MFMA layout: lane
@@ -533,9 +538,9 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmA
         const int r = 32 * FN * wn + 32 * f;
         bv[f] = km_frag(B + (r >> 7) * 1024, r & 127, kk, lane);
       }
+      // k rows past K hold copies of row K - 1: zeroing them in one operand
+      // removes their products.
       if (16 * kk + 16 > krem) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) av[i] = mask_k(av[i], kk, h, krem);
 #pragma unroll
         for (int f = 0; f < FN; ++f) bv[f] = mask_k(bv[f], kk, h, krem);
       }
