@@ -450,16 +450,36 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmA
     const char* abase;
     const char* bbase;
   };
-  auto tile_at = [&](int pos) {
-    Tile t{};
+  // Walk of the block's tiles (positions pos, pos + pstep, ... of its XCD's
+  // run) as a cursor (e, m tile, n tile): a step adds the stride's fixed
+  // decomposition with carries, so no division runs per tile.
+  struct Cursor {
+    int pos, e, mt, nt;
+  };
+  const int dn = pstep % ntn, dm = (pstep / ntn) % mtn, de = pstep / (ntn * mtn);
+  auto cursor_at = [&](int pos) {
     const int L = xcd * per_xcd + pos;
-    t.valid = pos < per_xcd && L < total;
+    const int e = L / (mtn * ntn), local = L - e * mtn * ntn;
+    return Cursor{pos, e, local / ntn, local % ntn};
+  };
+  auto step = [&](Cursor c) {
+    c.pos += pstep;
+    c.nt += dn;
+    int carry = c.nt >= ntn;
+    c.nt -= carry ? ntn : 0;
+    c.mt += dm + carry;
+    carry = c.mt >= mtn;
+    c.mt -= carry ? mtn : 0;
+    c.e += de + carry;
+    return c;
+  };
+  auto tile_at = [&](const Cursor& c) {
+    Tile t{};
+    t.valid = c.pos < per_xcd && xcd * per_xcd + c.pos < total;
     if (!t.valid) return t;
-    t.e = L / (mtn * ntn);
-    const int local = L - t.e * mtn * ntn;
-    const int mt = local / ntn;
-    t.m0 = mt * BM;
-    t.n0 = (local - mt * ntn) * BN;
+    t.e = c.e;
+    t.m0 = c.mt * BM;
+    t.n0 = c.nt * BN;
     t.K = s_cnt[t.e];
     t.nst = (t.K + BK - 1) / BK;
     const int off_e = s_off[t.e];
@@ -477,12 +497,12 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmA
             make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  // Position of the first tile at or after pos with slots (zero-filling the
-  // tiles before it when asked), or an invalid position.
-  auto next_with_slots = [&](int pos, bool zero_fill) {
-    for (;; pos += pstep) {
-      const Tile t = tile_at(pos);
-      if (!t.valid || t.nst > 0) return pos;
+  // The first tile at or after c with slots (zero-filling the tiles before
+  // it when asked), or an invalid one.
+  auto next_with_slots = [&](Cursor c, bool zero_fill) {
+    for (;; c = step(c)) {
+      const Tile t = tile_at(c);
+      if (!t.valid || t.nst > 0) return c;
       if (zero_fill) store_zero_tile(t);
     }
   };
@@ -557,12 +577,13 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmA
     s_off[j] = g.offsets[j];
   }
   __syncthreads();
-  int cur_pos = next_with_slots((int)(blockIdx.x >> 3), true);
-  Tile cur = tile_at(cur_pos);
+  Cursor cur_c = next_with_slots(cursor_at((int)(blockIdx.x >> 3)), true);
+  Tile cur = tile_at(cur_c);
   if (!cur.valid) return;  // block-uniform
   // The stream: stage number n of the block goes into slot n & 1; `la` is
-  // the next stage to issue (tile la_t at la_pos, stage la_s).
-  int la_pos = cur_pos, la_s = 0;
+  // the next stage to issue (tile la_t at cursor la_c, stage la_s).
+  Cursor la_c = cur_c;
+  int la_s = 0;
   Tile la_t = cur;
   int issued = 0;
   auto issue_next = [&]() {
@@ -570,8 +591,8 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmA
     issue(la_t, la_s, issued & 1);
     ++issued;
     if (++la_s >= la_t.nst) {
-      la_pos = next_with_slots(la_pos + pstep, true);
-      la_t = tile_at(la_pos);
+      la_c = next_with_slots(step(la_c), true);
+      la_t = tile_at(la_c);
       la_s = 0;
     }
   };
@@ -608,8 +629,8 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_stream_kernel(BwdGemmA
                                     {acc[2 * i2 + 1][2 * f2], acc[2 * i2 + 1][2 * f2 + 1]}};
         store_subtile<false>(sub, st, lane, obase, g.c_ld, rlim - r0, g.N - c0);
       }
-    cur_pos = next_with_slots(cur_pos + pstep, false);
-    cur = tile_at(cur_pos);
+    cur_c = next_with_slots(step(cur_c), false);
+    cur = tile_at(cur_c);
     if (!cur.valid) break;  // block-uniform; nothing is left in flight but stores
   }
 }
