@@ -88,7 +88,7 @@ def bwd_stage_of_kernel(name):
     """Map a kernel symbol of a backward-only run to its backward stage."""
     if "gemm_big_dma_kernel<true, false, true>" in name:
         return "u_silu"
-    for kname in ("bwd_gemm_kernel<", "bwd_wgrad_stream_kernel<"):
+    for kname in ("bwd_dgrad_kernel<", "bwd_wgrad_stream_kernel<", "bwd_wgrad_f32_kernel<"):
         if kname in name:
             op = int(name.split(kname)[1].split(">")[0].split(",")[-1])
             return BWD_OPS.get(op)

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void bwd_router_dz_kernel(const float* __restr
 // W_r's planes stacked to match dzp: wsp[s Ep + i][c] for segments s = 0..5
 // = planes (hi, mid, hi, lo, hi, mid) of W_r[i][c], rows i >= E zero. Thread
 // 0 also writes the one-group metadata of the two router-gradient GEMMs:
-// rg = {T, 0, 0, ceil(T / 128), 3 T, 0} (counts, offsets and tile prefix of
+// rg = {T, 0, 0, ceil(T / kBwdTileM), 3 T, 0} (counts, offsets and tile prefix of
 // dx_r; counts and offsets of dW_r).
 __global__ __launch_bounds__(256) void router_w_split_kernel(const float* __restrict__ wr, int E,
                                                              int Ep, int d, int T,

@@ -4,23 +4,23 @@
 //   C_e[m][n] = sum_k A_e(m, k) * B_e(n, k)   for every FFN expert e
 //
 // Two modes:
-//   dgrad: M = the expert's slot count. A is a matrix of slot rows stored
-//     k-contiguous (the gathered dy rows, or dU); B is the expert's weight
-//     matrix read i-contiguous (W2 for W2^T dy, W13 for dU W13; the
-//     k-contiguous form is supported too). Output rows are slot rows. The
-//     router's dz W_r runs in this mode as one group of T rows.
-//   wgrad: K = the expert's slot count. A and B are slot-row matrices read
+//   dgrad (bwd_dgrad_kernel): M = the expert's slot count. A is a matrix of
+//     slot rows stored k-contiguous (the gathered dy rows, or dU); B is the
+//     expert's weight matrix read i-contiguous (W2 for W2^T dy, W13 for
+//     dU W13). Output rows are slot rows. The router's dz W_r runs in this
+//     mode as one group of T rows.
+//   wgrad (bwd_wgrad_stream_kernel, bf16 out; bwd_wgrad_f32_kernel, fp32
+//     out): K = the expert's slot count. A and B are slot-row matrices read
 //     i-contiguous (element (i, k) at row k, column i): dW2 = dY^T (g h),
 //     dW13 = dU^T X. Output rows are rows of the expert's gradient matrix;
 //     an expert without slots gets zeros. The router's dz^T x runs in this
-//     mode as one group of 3T plane rows.
+//     mode (fp32) as one group of 3T plane rows.
 //
 // Tiles of BM x BN (per wave FM x FN fragments of 32 x 32), k stages of 64
 // moved HBM/L2 -> LDS by global_load_lds_dwordx4 (one instruction fills
-// 1 KB of LDS) in a ring of NSLOT stages, as in the forward's large-M kernel:
-// all slots are filled at the start of a tile; per stage, wait for this
-// wave's copies of the stage, a raw barrier, queue the next stage into the
-// slot just freed, multiply.
+// 1 KB of LDS) in a ring of stages, as in the forward's large-M kernel: per
+// stage, wait for this wave's copies of the stage, a raw barrier, queue the
+// next stage into the slot just freed, multiply.
 //
 // LDS tile forms, both conflict-free for 16-lane groups:
 //   k-contiguous [rows][64 k]: 128-byte rows, chunk c of row r at
@@ -37,6 +37,7 @@
 // n tile) (wgrad), so the M tiles of one weight tile, and all tiles of one
 // expert's operands, meet in one L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -148,23 +149,23 @@ __device__ __forceinline__ bf16x8_t mask_k(bf16x8_t v, int kk, int h, int krem) 
   return *reinterpret_cast<bf16x8_t*>(&u);
 }
 
-// Store one wave's 64 x 64 output sub-tile (the transposed-MFMA layout: lane
-// holds row 32 i + lane % 32, columns 32 f + 8 q + 4 (lane / 32) + [0, 4))
-// through LDS, so each global store instruction writes whole rows: 128 bytes
-// per row (bf16, 8 rows per instruction) or 256 bytes (fp32, 4 rows).
-// st: this wave's 8 KB (bf16) or 16 KB (fp32) of LDS; rows of 8 or 16
+// Store one wave's (32 NI) x 64 output sub-tile (the transposed-MFMA layout:
+// lane holds row 32 i + lane % 32, columns 32 f + 8 q + 4 (lane / 32) +
+// [0, 4)) through LDS, so each global store instruction writes whole rows:
+// 128 bytes per row (bf16, 8 rows per instruction) or 256 bytes (fp32, 4
+// rows). st: this wave's 4 NI KB (bf16) or 8 NI KB (fp32) of LDS; rows of 8 or 16
 // chunks, chunk c of row r at c ^ ((r >> 1) & 7) (bf16) or c ^ (r & 15)
 // (fp32), conflict-free for the writes and the row-major reads. obase:
 // element (0, 0) of the sub-tile in the output, ld its row stride; rows at or
 // past rvalid and columns at or past cvalid are not written.
-template <bool F32>
-__device__ __forceinline__ void store_subtile(const f32x16_t (&acc)[2][2], uint4* st, int lane,
+template <bool F32, int NI = 2>
+__device__ __forceinline__ void store_subtile(const f32x16_t (&acc)[NI][2], uint4* st, int lane,
                                               char* obase, long long ld, int rvalid, int cvalid) {
   constexpr int RC = F32 ? 16 : 8;  // 16-byte chunks per sub-tile row
   constexpr int ESZ = F32 ? 4 : 2;
   const int h = lane >> 5, lr = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -183,7 +184,7 @@ __device__ __forceinline__ void store_subtile(const f32x16_t (&acc)[2][2], uint4
       }
   constexpr int RPI = 64 / RC;  // rows per read instruction
 #pragma unroll
-  for (int j = 0; j < 64 / RPI; ++j) {
+  for (int j = 0; j < 32 * NI / RPI; ++j) {
     const int r = RPI * j + lane / RC, c = lane % RC;
     const uint4 v = st[r * RC + (F32 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)))];
     const int col = c * (16 / ESZ);
@@ -194,138 +195,82 @@ __device__ __forceinline__ void store_subtile(const f32x16_t (&acc)[2][2], uint4
 
 }  // namespace
 
-// OP (a BwdOp) only names the launch, so profiles tell the GEMMs apart.
-template <bool WGRAD, bool B_KM, bool OUT_F32, int WM, int WN, int FM, int FN, int NSLOT, int OP>
-__global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
-  constexpr bool A_KM = WGRAD;
-  constexpr bool BKM = WGRAD || B_KM;
+// The router's weight gradient dW_r = dz^T x (fp32 output): the wgrad form
+// with one group (counts[0] = K rows, M and N fixed), both operands read
+// i-contiguous from slot-row matrices. Few tiles and a long k: a ring of
+// NSLOT stages per tile, all slots filled at the start; per stage, wait for
+// this wave's copies of the stage, a raw barrier, queue the next stage into
+// the slot just freed, multiply. OP (a BwdOp) only names the launch, so
+// profiles tell the GEMMs apart.
+template <int WM, int WN, int FM, int FN, int NSLOT, int OP>
+__global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_f32_kernel(BwdGemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;  // wave tile (32 FM) x (32 FN)
   static_assert(FM % 2 == 0 && FN % 2 == 0, "stores go by 64 x 64 sub-tiles");
-  static_assert(WGRAD || BM == kBwdTileM, "dgrad M tiles are those of the tile prefix");
   constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per stage
   constexpr int SLOT = A_CH + B_CH;
   constexpr int NB = SLOT / 64;                // 1 KB copy blocks per stage
   constexpr int CPW = NB / NW;                 // copies per wave per stage
   constexpr int JA = (A_CH / 64) / NW;         // the first JA of them fill A
   static_assert(NB % NW == 0 && (A_CH / 64) % NW == 0, "copy blocks must split evenly");
-  static_assert(NW * (OUT_F32 ? 1024 : 512) <= NSLOT * SLOT, "epilogue staging fits in the ring");
+  static_assert(NW * 1024 <= NSLOT * SLOT, "epilogue staging fits in the ring");
   static_assert((NSLOT - 1) * (NB / NW) <= 24, "vmcnt range of the waits");
-  static_assert(!A_KM || BM % 128 == 0, "i-contiguous tiles are 128 wide");
-  static_assert(!BKM || BN % 128 == 0, "i-contiguous tiles are 128 wide");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "i-contiguous tiles are 128 wide");
   __shared__ uint4 lds[NSLOT * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int h = lane >> 5, lr = lane & 31;
 
-  // ---- work item -> (expert, m tile, n tile) ----
-  const int ntn = (g.N + BN - 1) / BN;
-  int total;
-  if (WGRAD) total = g.n_ffn * ((g.M + BM - 1) / BM) * ntn;
-  else total = g.tile_prefix[g.n_ffn] * ntn;
+  // ---- work item -> (expert, m tile, n tile), per-XCD contiguous runs ----
+  const int ntn = (g.N + BN - 1) / BN, mtn = (g.M + BM - 1) / BM;
+  const int total = g.n_ffn * mtn * ntn;
   const int per_xcd = (total + 7) >> 3;
   const int pos = blockIdx.x >> 3;
   if (pos >= per_xcd) return;
   const int L = (int)(blockIdx.x & 7) * per_xcd + pos;
   if (L >= total) return;
-  int e, mt, nt;
-  if (WGRAD) {
-    const int mtn = (g.M + BM - 1) / BM;
-    e = L / (mtn * ntn);
-    const int local = L - e * mtn * ntn;
-    mt = local / ntn;
-    nt = local - mt * ntn;
-  } else {
-    int lo = 0, hi = g.n_ffn - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_prefix[mid] * ntn <= L) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-    const int mtiles = g.tile_prefix[e + 1] - g.tile_prefix[e];
-    const int local = L - g.tile_prefix[e] * ntn;
-    nt = local / mtiles;
-    mt = local - nt * mtiles;
-  }
-  const int cnt = g.counts[e];
+  const int e = L / (mtn * ntn);
+  const int local = L - e * mtn * ntn;
+  const int mt = local / ntn, nt = local - mt * ntn;
   const int off_e = g.offsets[e];
-  const int M = WGRAD ? g.M : cnt;
-  const int N = g.N;
-  const int K = WGRAD ? cnt : g.K;
+  const int M = g.M, N = g.N, K = g.counts[e];
   const int m0 = mt * BM, n0 = nt * BN;
-
-  // Operand bases (bytes): A slot rows start at the expert's first slot; B
-  // is the expert's weight matrix (dgrad) or its slot rows (wgrad).
   const char* abase = reinterpret_cast<const char*>(g.a) + (size_t)off_e * g.a_ld * 2;
-  const char* bbase = reinterpret_cast<const char*>(g.b) +
-                      (WGRAD ? (size_t)off_e * g.b_ld * 2 : (size_t)e * g.b_estride * 2);
+  const char* bbase = reinterpret_cast<const char*>(g.b) + (size_t)off_e * g.b_ld * 2;
   const int nst = (K + BK - 1) / BK;
-  const bool half_tail = !WGRAD && (K % BK) != 0;  // dgrad: K is a multiple of 32
 
   // ---- per-lane copy descriptors (stage independent) ----
-  // Copy j of this wave fills 1 KB block wave + NW j of the stage: A blocks
-  // first, then B. k-contiguous block: rows 8 b + lane / 8, chunk lane % 8
-  // of the swizzled row (the lane loads the logical chunk placed there).
-  // i-contiguous block: sub-tile b / 16, k rows 4 (b % 16) + lane / 16.
-  uint32_t voff[CPW];   // byte offset from the stage's scalar base
-  int krow[CPW];        // i-contiguous: k row within the stage
-  bool use[CPW];
-  int kcc = 0;          // k-contiguous: logical chunk of this lane (same for all its blocks)
+  // Copy j of this wave fills 1 KB block b = wave + NW j of the stage (A
+  // blocks first, then B): sub-tile b / 16, k rows 4 (b % 16) + lane / 16,
+  // swizzled 64-byte window of the lane.
+  uint32_t voff[CPW];
+  int krow[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const bool isA = j < JA;
     const int b = isA ? wave + NW * j : wave + NW * j - A_CH / 64;
-    const bool km = isA ? A_KM : BKM;
-    const long long ld = isA ? g.a_ld : g.b_ld;
-    use[j] = true;
-    krow[j] = 0;
-    if (!km) {
-      const int row = 8 * b + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      kcc = c;
-      // rows: A slot rows m0 + row (< M), B weight rows n0 + row (< N)
-      const int lim = isA ? M - m0 : N - n0;
-      use[j] = 8 * b < lim;
-      const int rr = (isA ? m0 : n0) + (row < lim ? row : (lim > 0 ? lim - 1 : 0));
-      voff[j] = (uint32_t)((size_t)rr * ld * 2 + 16 * c);
-    } else {
-      const int q = b >> 4, bb = b & 15;
-      const int k = 4 * bb + (lane >> 4), pc = lane & 15;
-      const int c = ((((pc >> 2) ^ (k & 3))) << 2) | (pc & 3);
-      const int ext = isA ? M : N;
-      int col = (isA ? m0 : n0) + 128 * q + 8 * c;
-      if (col > ext - 8) col = ext - 8;
-      krow[j] = k;
-      voff[j] = (uint32_t)(col * 2);
-    }
+    const int q = b >> 4, bb = b & 15;
+    const int k = 4 * bb + (lane >> 4), pc = lane & 15;
+    const int c = ((((pc >> 2) ^ (k & 3))) << 2) | (pc & 3);
+    const int ext = isA ? M : N;
+    int col = (isA ? m0 : n0) + 128 * q + 8 * c;
+    if (col > ext - 8) col = ext - 8;
+    krow[j] = k;
+    voff[j] = (uint32_t)(col * 2);
   }
-  int per_stage = 0;
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) per_stage += (int)use[j];
 
   auto issue = [&](int s) {
     const int k0 = s * BK;
-    const int kmax = K - 1 - k0;  // i-contiguous rows past K re-load row K - 1
-    // dgrad tail stage of an odd multiple of 32: k-contiguous chunks 4..7 do
-    // not exist; those lanes load chunk c - 4 (64 bytes back), which no MFMA reads.
-    const uint32_t back = (half_tail && s == nst - 1 && kcc >= 4) ? 64u : 0u;
+    const int kmax = K - 1 - k0;  // rows past K re-load row K - 1
     uint4* slot = lds + (s % NSLOT) * SLOT;
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-      if (!use[j]) continue;
       const bool isA = j < JA;
-      const int b = wave + NW * j;  // block within the slot (A blocks first)
-      const bool km = isA ? A_KM : BKM;
       const long long ld = isA ? g.a_ld : g.b_ld;
-      const char* base = isA ? abase : bbase;
-      if (!km) {
-        bdma16(base + 2 * (size_t)k0, voff[j] - back, slot + 64 * b);
-      } else {
-        const int k = krow[j] < kmax ? krow[j] : kmax;
-        bdma16(base + (size_t)k0 * ld * 2, voff[j] + (uint32_t)(k * ld * 2), slot + 64 * b);
-      }
+      const int k = krow[j] < kmax ? krow[j] : kmax;
+      bdma16((isA ? abase : bbase) + (size_t)k0 * ld * 2, voff[j] + (uint32_t)(k * ld * 2),
+             slot + 64 * (wave + NW * j));
     }
   };
 
@@ -342,8 +287,9 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
   auto compute = [&](int s) {
     const uint4* A = lds + (s % NSLOT) * SLOT;
     const uint4* B = A + A_CH;
-    const int krem = K - s * BK;  // valid k in this stage (wgrad tail)
-    const int nkk = WGRAD ? min(4, (krem + 15) >> 4) : ((half_tail && s == nst - 1) ? 2 : 4);
+    const int krem = K - s * BK;  // valid k in this stage
+    const int nkk = min(4, (krem + 15) >> 4);
+    const int h = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk >= nkk) break;
@@ -351,18 +297,16 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = 32 * FM * wm + 32 * i;
-        av[i] = A_KM ? km_frag(A + (r >> 7) * 1024, r & 127, kk, lane)
-                     : as_bf16x8(A[kc_off(r + lr, 2 * kk + h)]);
+        av[i] = km_frag(A + (r >> 7) * 1024, r & 127, kk, lane);
       }
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
         const int r = 32 * FN * wn + 32 * f;
-        bv[f] = BKM ? km_frag(B + (r >> 7) * 1024, r & 127, kk, lane)
-                    : as_bf16x8(B[kc_off(r + lr, 2 * kk + h)]);
+        bv[f] = km_frag(B + (r >> 7) * 1024, r & 127, kk, lane);
       }
-      if (WGRAD && 16 * kk + 16 > krem) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) av[i] = mask_k(av[i], kk, h, krem);
+      // k rows past K hold copies of row K - 1: zeroing them in one operand
+      // removes their products.
+      if (16 * kk + 16 > krem) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) bv[f] = mask_k(bv[f], kk, h, krem);
       }
@@ -374,9 +318,9 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
     }
   };
 
-  // Every slot is free at the start, so NSLOT stages go out at once (a tile
-  // of at most NSLOT stages waits for one round trip); from stage 1 on, the
-  // next stage goes into the slot stage s - 1 has just released.
+  // Every slot is free at the start, so NSLOT stages go out at once; from
+  // stage 1 on, the next stage goes into the slot stage s - 1 has released.
+  const int per_stage = CPW;
   int issued = min(NSLOT, nst);
   for (int s = 0; s < issued; ++s) issue(s);
   for (int s = 0; s < nst; ++s) {
@@ -388,18 +332,192 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_gemm_kernel(BwdGemmArgs g) {
 
   // ---- epilogue through LDS (the ring is free once every wave is done) ----
   braw_barrier();
+  const int rlim = min(M, g.m_store);
 #pragma unroll
   for (int i2 = 0; i2 < FM / 2; ++i2)
 #pragma unroll
     for (int f2 = 0; f2 < FN / 2; ++f2) {
       const int r0 = m0 + 32 * FM * wm + 64 * i2, c0 = n0 + 32 * FN * wn + 64 * f2;
-      const long long orow = WGRAD ? (long long)e * g.M + r0 : (long long)off_e + r0;
-      char* obase = static_cast<char*>(g.c) + (orow * g.c_ld + c0) * (OUT_F32 ? 4 : 2);
+      char* obase = static_cast<char*>(g.c) + (((long long)e * M + r0) * g.c_ld + c0) * 4;
       const f32x16_t sub[2][2] = {{acc[2 * i2][2 * f2], acc[2 * i2][2 * f2 + 1]},
                                   {acc[2 * i2 + 1][2 * f2], acc[2 * i2 + 1][2 * f2 + 1]}};
-      store_subtile<OUT_F32>(sub, lds + wave * (OUT_F32 ? 1024 : 512), lane, obase, g.c_ld,
-                             (WGRAD ? min(M, g.m_store) : M) - r0, N - c0);
+      store_subtile<true>(sub, lds + wave * 1024, lane, obase, g.c_ld, rlim - r0, N - c0);
     }
+}
+
+// Data gradients (W2^T dy, dU W13, the router's dz W_r): C[m][n] = sum_k
+// A(m, k) B_e(n, k) with A slot rows read k-contiguous and the weights read
+// i-contiguous. An M tile holds up to kBwdTileM (256) slot rows, so at a
+// prefill batch (about 128 rows per expert, rarely past 170) every expert's
+// rows share one tile and each weight tile is multiplied once. 2 x 4 waves
+// over a 256 x 256 tile: wave (wm, wn) holds the 32-row fragments 2 j + wm
+// (j < 4) and 64 columns; only the fragments that hold rows are multiplied
+// (the k loop is instantiated per active count, straight-line code). A stage
+// is the tile's rows in whole 32-row fragments (rows past the count re-load
+// the last row) and two [64 k][128 i] weight sub-tiles; the ring holds as
+// many stages as fit in 160 KB of LDS, up to 3 (3 for up to 160 rows).
+template <bool OUT_F32, int OP>
+__global__ __launch_bounds__(512) void bwd_dgrad_kernel(BwdGemmArgs g) {
+  constexpr int NW = 8, WN = 4, FM = 4, FN = 2;
+  constexpr int BM = kBwdTileM, BN = kBwdTileNDgrad;
+  static_assert(BM == 32 * FM * 2 && BN == 32 * FN * WN, "256 x 256 tiles");
+  constexpr int B_CH = BN * 8;     // weight sub-tiles per stage (16-byte chunks)
+  constexpr int LDS_CH = 10240;    // 160 KB
+  constexpr int MAX_SLOTS = 3;
+  constexpr int ACPW = BM / 8 / NW;  // A copy groups per wave, at most (4)
+  constexpr int BCPW = B_CH / 64 / NW;  // weight copies per wave (4)
+  static_assert(NW * (OUT_F32 ? 512 : 256) <= LDS_CH, "epilogue staging fits");
+  __shared__ uint4 lds[LDS_CH];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int h = lane >> 5, lr = lane & 31;
+
+  // ---- work item -> (expert, n tile, m tile), per-XCD contiguous runs ----
+  const int ntn = (g.N + BN - 1) / BN;
+  const int total = g.tile_prefix[g.n_ffn] * ntn;
+  const int per_xcd = (total + 7) >> 3;
+  const int pos = blockIdx.x >> 3;
+  if (pos >= per_xcd) return;
+  const int L = (int)(blockIdx.x & 7) * per_xcd + pos;
+  if (L >= total) return;
+  int lo = 0, hi = g.n_ffn - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.tile_prefix[mid] * ntn <= L) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int mtiles = g.tile_prefix[e + 1] - g.tile_prefix[e];
+  const int local = L - g.tile_prefix[e] * ntn;
+  const int nt = local / mtiles, mt = local - nt * mtiles;
+  const int off_e = g.offsets[e];
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int rows = min(BM, g.counts[e] - m0);  // >= 1: tiles cover counts exactly
+  const int N = g.N, K = g.K;
+  const int nfr = (rows + 31) >> 5;            // 32-row fragments holding rows
+  const int a_ch = nfr * 256;                  // A chunks per stage (8 rows per 64)
+  const int slot = a_ch + B_CH;
+  const int nslots = min(MAX_SLOTS, LDS_CH / slot);
+  const int nst = (K + BK - 1) / BK;
+  const bool half_tail = (K % BK) != 0;        // K is a multiple of 32
+
+  const char* abase = reinterpret_cast<const char*>(g.a) + (size_t)off_e * g.a_ld * 2;
+  const char* bbase = reinterpret_cast<const char*>(g.b) + (size_t)e * g.b_estride * 2;
+
+  // ---- per-lane copy descriptors ----
+  // A group j of this wave: 8 rows 8 (wave + NW j) + lane / 8 of the tile,
+  // chunk lane % 8 of the swizzled row (holding logical chunk c). Weight copy
+  // j: 1 KB block b = wave + NW j of the stage, sub-tile b / 16, k row
+  // 4 (b % 16) + lane / 16, swizzled 64-byte window of the lane.
+  uint32_t aoff[ACPW];
+  const int a_groups = nfr * 4;
+  int acnt = 0, kcc = 0;  // kcc: the logical chunk (the same for all groups: NW is even)
+#pragma unroll
+  for (int j = 0; j < ACPW; ++j) {
+    const int row = 8 * (wave + NW * j) + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int rr = m0 + min(row, rows - 1);
+    aoff[j] = (uint32_t)((size_t)rr * g.a_ld * 2 + 16 * c);
+    acnt += (wave + NW * j < a_groups) ? 1 : 0;
+    kcc = c;
+  }
+  uint32_t boff[BCPW];
+  int krow[BCPW];
+#pragma unroll
+  for (int j = 0; j < BCPW; ++j) {
+    const int b = wave + NW * j;
+    const int q = b >> 4, bb = b & 15;
+    const int k = 4 * bb + (lane >> 4), pc = lane & 15;
+    const int c = ((((pc >> 2) ^ (k & 3))) << 2) | (pc & 3);
+    int col = n0 + 128 * q + 8 * c;
+    if (col > N - 8) col = N - 8;
+    krow[j] = k;
+    boff[j] = (uint32_t)(col * 2);
+  }
+  const int per_stage = acnt + BCPW;
+
+  auto issue = [&](int s, int si) {
+    const int k0 = s * BK;
+    const int kmax = K - 1 - k0;  // weight rows past K re-load row K - 1
+    // tail stage of an odd multiple of 32: chunks 4..7 of the A rows do not
+    // exist; those lanes load chunk c - 4 (64 bytes back), which no MFMA reads.
+    const uint32_t back = (half_tail && s == nst - 1 && kcc >= 4) ? 64u : 0u;
+    uint4* dst = lds + si * slot;
+#pragma unroll
+    for (int j = 0; j < ACPW; ++j)
+      if (wave + NW * j < a_groups) bdma16(abase + 2 * (size_t)k0, aoff[j] - back, dst + 64 * (wave + NW * j));
+#pragma unroll
+    for (int j = 0; j < BCPW; ++j) {
+      const int k = krow[j] < kmax ? krow[j] : kmax;
+      bdma16(bbase + (size_t)k0 * g.b_ld * 2, boff[j] + (uint32_t)(k * g.b_ld * 2),
+             dst + a_ch + 64 * (wave + NW * j));
+    }
+  };
+
+  const int nact = __builtin_amdgcn_readfirstlane(max(0, min(FM, (nfr - wm + 1) >> 1)));
+  bwait_vmcnt<0>();  // the loads of the setup have landed
+
+  auto run = [&](auto NA_c) {
+    constexpr int NA = decltype(NA_c)::value;
+    f32x16_t acc[NA > 0 ? NA : 1][FN];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.f;
+    int issued = min(nslots, nst);
+    for (int s = 0; s < issued; ++s) issue(s, s);
+    int si = 0;  // slot of stage s
+    for (int s = 0; s < nst; ++s) {
+      bwait_vmcnt_upto(per_stage * (issued - 1 - s));
+      braw_barrier();
+      if (s >= 1 && issued < nst) {  // into the slot stage s - 1 released
+        issue(issued, si == 0 ? nslots - 1 : si - 1);
+        ++issued;
+      }
+      const uint4* A = lds + si * slot;
+      const uint4* B = A + a_ch;
+      const int nkk = (half_tail && s == nst - 1) ? 2 : 4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk >= nkk) break;
+        bf16x8_t av[NA > 0 ? NA : 1], bv[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int r = 32 * FN * wn + 32 * f;
+          bv[f] = km_frag(B + (r >> 7) * 1024, r & 127, kk, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < NA; ++i) av[i] = as_bf16x8(A[kc_off(32 * (2 * i + wm) + lr, 2 * kk + h)]);
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[f], av[i], acc[i][f], 0, 0, 0);
+      }
+      si = si + 1 == nslots ? 0 : si + 1;
+    }
+    // ---- epilogue through LDS (the ring is free once every wave is done) ----
+    braw_barrier();
+    uint4* st = lds + wave * (OUT_F32 ? 512 : 256);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int r0 = 32 * (2 * i + wm), c0 = n0 + 64 * wn;
+      char* obase = static_cast<char*>(g.c) +
+                    (((long long)off_e + m0 + r0) * g.c_ld + c0) * (OUT_F32 ? 4 : 2);
+      const f32x16_t sub[1][2] = {{acc[i][0], acc[i][1]}};
+      store_subtile<OUT_F32, 1>(sub, st, lane, obase, g.c_ld, rows - r0, N - c0);
+    }
+  };
+  switch (nact) {
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+  }
 }
 
 // Weight-gradient GEMMs (bf16 outputs dW2, dW13), persistent: one block per
@@ -660,7 +778,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 }
 
 // Grid of the dgrad launch: an upper bound of the work items (every expert's
-// M tiles at 128 rows, over all slots) rounded for the per-XCD layout.
+// M tiles of kBwdTileM rows, over all slots) rounded for the per-XCD layout.
 int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols) {
   const long long items = (smax / kBwdTileM + n_ffn) * ((n_cols + kBwdTileNDgrad - 1) / kBwdTileNDgrad);
   return (int)std::min<long long>(items + 8, 1ll << 30);
@@ -684,13 +802,10 @@ int bwd_wgrad_grid(int n_ffn, int M, int N) {
 }
 
 void launch_bwd_dgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
-  static_assert(kBwdTileM == 128 && kBwdTileNDgrad == 256, "dgrad tile");
   switch (op) {
-    case kBwdQ: bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdQ><<<grid, 512, 0, s>>>(g); break;
-    case kBwdDx: bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdDx><<<grid, 512, 0, s>>>(g); break;
-    default:
-      bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, kBwdRouterDx><<<grid, 512, 0, s>>>(g);
-      break;
+    case kBwdQ: bwd_dgrad_kernel<true, kBwdQ><<<grid, 512, 0, s>>>(g); break;
+    case kBwdDx: bwd_dgrad_kernel<true, kBwdDx><<<grid, 512, 0, s>>>(g); break;
+    default: bwd_dgrad_kernel<true, kBwdRouterDx><<<grid, 512, 0, s>>>(g); break;
   }
 }
 void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
@@ -701,7 +816,7 @@ void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
 }
 void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s) {
   const long long items = (long long)g.n_ffn * ((g.M + 127) / 128) * ((g.N + 127) / 128);
-  bwd_gemm_kernel<true, true, true, 2, 2, 2, 2, 3, kBwdRouterDw>
+  bwd_wgrad_f32_kernel<2, 2, 2, 2, 3, kBwdRouterDw>
       <<<(int)std::min<long long>(items + 8, 1ll << 30), 256, 0, s>>>(g);
 }
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,

@@ -80,10 +80,10 @@ void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, d
 
 // Backward grouped GEMMs: C_e[m][n] = sum_k A_e(m, k) B_e(n, k) per FFN
 // expert (see bwd_gemm.hip). dgrad: A = slot rows (k-contiguous), B = the
-// expert's weight matrix, M = the expert's slot count, output rows = slot
-// rows. wgrad: A and B = slot rows read i-contiguous, K = the slot count,
-// output rows e * M + m.
-constexpr int kBwdTileM = 128;       // rows per dgrad M tile (slot rows)
+// expert's weight matrix read i-contiguous, M = the expert's slot count,
+// output rows = slot rows (fp32). wgrad: A and B = slot rows read
+// i-contiguous, K = the slot count, output rows e * M + m.
+constexpr int kBwdTileM = 256;       // rows per dgrad M tile (slot rows)
 constexpr int kBwdTileNDgrad = 256;  // columns per dgrad tile
 struct BwdGemmArgs {
   const uint16_t* a;       // A base (bf16): slot-row matrix, row 0 = slot row 0

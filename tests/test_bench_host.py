@@ -64,10 +64,11 @@ def test_stage_maps():
         == "down_small"
     assert bench.stage_of_kernel("lcmoe::combine_kernel(unsigned short const*)") == "combine"
     assert bench.bwd_stage_of_kernel(
-        "void lcmoe::bwd_gemm_kernel<true, true, false, 2, 4, 4, 2, 2, 5>(lcmoe::BwdGemmArgs)") == "dw13"
+        "void lcmoe::bwd_dgrad_kernel<true, 3>(lcmoe::BwdGemmArgs)") == "dx_rows"
     assert bench.bwd_stage_of_kernel(
-        "void lcmoe::bwd_gemm_kernel<false, true, true, 2, 4, 2, 2, 3, 3>(lcmoe::BwdGemmArgs)") \
-        == "dx_rows"
+        "void lcmoe::bwd_dgrad_kernel<true, 2>(lcmoe::BwdGemmArgs)") == "w2t_dy"
+    assert bench.bwd_stage_of_kernel(
+        "void lcmoe::bwd_wgrad_f32_kernel<2, 2, 2, 2, 3, 7>(lcmoe::BwdGemmArgs)") == "router_grads"
     assert bench.bwd_stage_of_kernel(
         "void lcmoe::bwd_wgrad_stream_kernel<2, 4, 4, 2, 5>(lcmoe::BwdGemmArgs)") == "dw13"
     assert bench.bwd_stage_of_kernel(
