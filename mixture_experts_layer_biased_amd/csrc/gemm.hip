@@ -311,12 +311,15 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * 4 + (chunk ^ ((row >> 2) & 3));
 }
 
-// The ring lives in one 144 KB LDS array. A slot holds the x rows of the
-// tile (8-row groups, 128 B per row) followed by the weight tile; the slot
-// count is what fits for the tile's actual row count, capped at 3.
+// The ring lives in one 160 KB LDS array (all of a CU's LDS). A slot holds
+// the x rows of the tile (8-row groups, 128 B per row) followed by the
+// weight tile; the slot count is what fits for the tile's actual row count,
+// capped at 3: with bf16 weights 3 slots up to 168 rows, which covers an
+// expert's rows at a prefill batch (about 128 +- 12); in 144 KB, tiles past
+// 128 rows had 2.
 template <bool FP8>
 struct DmaTile {
-  static constexpr int LDS_CHUNKS = 9216;                   // 144 KB
+  static constexpr int LDS_CHUNKS = 10240;                  // 160 KB
   static constexpr int MAX_SLOTS = 3;
   static constexpr int B_CHUNKS = FP8 ? 256 * 4 : 256 * 8;  // weight tile, 16 or 32 KB
   static constexpr int AGROUPS = kBigTileRows / 8;          // 8-row copy groups of the x tile
