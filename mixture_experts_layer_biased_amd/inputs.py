@@ -174,6 +174,30 @@ def make_layer(cfg, device):
                 w13_scale=w13_scale, w2_scale=w2_scale)
 
 
+def counted_routing_inputs(counts, d, device, seed):
+    """Tokens and a router that send exactly counts[e] tokens to expert e
+    (with top-1 selection and zero bias), in a seeded shuffled order.
+
+    W_r is the E x d identity (E <= d), so logit z_e of a token is its x
+    coordinate e, exact in fp32. Token t has x[choice_t] = 2 and every other
+    coordinate uniform in (-1, 1) rounded to bf16, so its only maximum is its
+    chosen expert. Returns x bf16 [T, d], W_r fp32 [E, d], bias fp32 [E] and
+    the chosen expert of every token (int64 [T]).
+    """
+    E = len(counts)
+    assert E <= d
+    g = _gen(device, seed, 11)
+    choice = torch.repeat_interleave(torch.arange(E, device=device),
+                                     torch.as_tensor(counts, device=device))
+    choice = choice[torch.randperm(choice.numel(), generator=g, device=device)]
+    T = choice.numel()
+    x = torch.rand(T, d, generator=g, device=device, dtype=torch.float32) * 2 - 1
+    x[torch.arange(T, device=device), choice] = 2.0
+    w = torch.zeros(E, d, device=device, dtype=torch.float32)
+    w[torch.arange(E, device=device), torch.arange(E, device=device)] = 1.0
+    return x.to(torch.bfloat16), w, torch.zeros(E, device=device), choice
+
+
 def exact_router_inputs(T, d, E, device, seed, dup_pairs=0):
     """Inputs on which every fp32 router logit is exact under any summation order.
 
