@@ -227,7 +227,8 @@ __global__ __launch_bounds__(256) void router_w_split_kernel(const float* __rest
 }
 
 // One block per token: dx_t = sum over its FFN slots (k order) of the dXs
-// rows + (sum over its zero slots of g) dy_t + dxr_t, fp32.
+// rows + (sum over its zero slots of g) dy_t + dxr_t, fp32. Four columns per
+// thread (16-byte loads and stores; d is a multiple of 32).
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dXs,
                                                      const uint16_t* __restrict__ dy,
                                                      const float* __restrict__ dxr,
@@ -245,13 +246,27 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   float gz = 0.f;
   for (int k = 0; k < K; ++k)
     if (srow[k] < 0) gz += sg[k];
-  for (int c = tid; c < d; c += 256) {
-    float v = 0.f;
+  for (int c = 4 * tid; c < d; c += 4 * 256) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < K; ++k)
-      if (srow[k] >= 0) v += dXs[(size_t)srow[k] * d + c];
-    v += gz * bf16_to_f32(dy[(size_t)t * d + c]);
-    v += dxr[(size_t)t * d + c];
-    dx[(size_t)t * d + c] = v;
+      if (srow[k] >= 0) {
+        const float4 r = *reinterpret_cast<const float4*>(dXs + (size_t)srow[k] * d + c);
+        v.x += r.x;
+        v.y += r.y;
+        v.z += r.z;
+        v.w += r.w;
+      }
+    const uint2 yb = *reinterpret_cast<const uint2*>(dy + (size_t)t * d + c);
+    const float4 xr = *reinterpret_cast<const float4*>(dxr + (size_t)t * d + c);
+    v.x += gz * bf16_lo(yb.x);
+    v.y += gz * bf16_hi(yb.x);
+    v.z += gz * bf16_lo(yb.y);
+    v.w += gz * bf16_hi(yb.y);
+    v.x += xr.x;
+    v.y += xr.y;
+    v.z += xr.z;
+    v.w += xr.w;
+    *reinterpret_cast<float4*>(dx + (size_t)t * d + c) = v;
   }
 }
 
