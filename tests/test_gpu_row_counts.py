@@ -10,8 +10,9 @@ the dgrad M tile (256 rows) and its ring (3 slots up to 160 rows), the
 weight-gradient k stages (64 slot rows), and an FFN expert with no rows
 (zero weight gradients). d = 128 is narrower than one 256-column dgrad
 tile; I = 160 makes the gate/up output and the W2^T dy product ragged and
-the down product's k an odd multiple of 32. Tolerances are those of the
-other parity tests.
+the down product's k an odd multiple of 32. The forward is also checked
+with fp8 weights and with fp8 weights and activations (their own kernels and
+ring geometry). Tolerances are those of the other parity tests.
 """
 import numpy as np
 import pytest
@@ -27,11 +28,17 @@ ZERO_COUNTS = [5, 0, 3, 7]
 SEED = 20261204
 
 
-def _layer():
+# fp8 weights need d and I multiples of 128 (the scale blocks); fp8
+# activations are checked at I >= 384, as in the other fp8-activation tests.
+INTER = {"bf16": 160, "fp8": 256, "fp8a8": 384}
+
+
+def _layer(wdtype="bf16"):
     counts = FFN_COUNTS + ZERO_COUNTS
-    cfg = inputs.CONFIGS["tiny"].with_(name="row_counts", d=128, inter=160, n_ffn=len(FFN_COUNTS),
-                                       n_zero=len(ZERO_COUNTS), k=1, tokens=sum(counts),
-                                       seed=SEED, bias_std=0.0, skew_frac=0.0, skew_factor=1.0)
+    cfg = inputs.CONFIGS["tiny"].with_(name=f"row_counts_{wdtype}", d=128, inter=INTER[wdtype],
+                                       n_ffn=len(FFN_COUNTS), n_zero=len(ZERO_COUNTS), k=1,
+                                       tokens=sum(counts), seed=SEED, bias_std=0.0, skew_frac=0.0,
+                                       skew_factor=1.0, wdtype=wdtype)
     L = inputs.make_layer(cfg, "cuda")
     x, w_r, bias, choice = inputs.counted_routing_inputs(counts, cfg.d, "cuda", SEED)
     L["w_router"], L["bias"] = w_r, bias
@@ -44,6 +51,16 @@ def test_counts_cover_the_boundaries():
     for lo, hi in [(32, 33), (64, 65), (128, 129), (160, 161), (168, 169), (256, 257), (320, 321)]:
         assert lo in c and hi in c
     assert 0 in c and max(c) > 320
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8a8"])
+def test_forward_fp8_at_row_count_boundaries(wdtype):
+    cfg, L, x, choice, counts = _layer(wdtype)
+    res = run_forward(cfg, L, x)
+    assert torch.equal(res["idx"][:, 0].long(), choice)
+    assert np.array_equal(res["counts"].cpu().numpy(), np.array(counts))
+    check_rows(cfg, L, x, res, np.arange(cfg.tokens), cache={})
 
 
 @pytest.mark.gpu
