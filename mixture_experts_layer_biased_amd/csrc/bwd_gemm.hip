@@ -816,7 +816,9 @@ void launch_bwd_wgrad(const BwdGemmArgs& g, BwdOp op, int grid, hipStream_t s) {
 }
 void launch_bwd_wgrad_f32(const BwdGemmArgs& g, hipStream_t s) {
   const long long items = (long long)g.n_ffn * ((g.M + 127) / 128) * ((g.N + 127) / 128);
-  bwd_wgrad_f32_kernel<2, 2, 2, 2, 3, kBwdRouterDw>
+  // Two slots (64 KB of LDS) so two blocks share a CU: the router's 288
+  // tiles at E = 768, d = 6144 then run in one round on 256 CUs.
+  bwd_wgrad_f32_kernel<2, 2, 2, 2, 2, kBwdRouterDw>
       <<<(int)std::min<long long>(items + 8, 1ll << 30), 256, 0, s>>>(g);
 }
 void launch_gather_rows(const uint16_t* x, const uint16_t* dy, const int* perm, const int* s_dev,
