@@ -53,6 +53,18 @@ def test_counts_cover_the_boundaries():
     assert 0 in c and max(c) > 320
 
 
+def test_counted_routing_inputs_on_cpu():
+    # host-only: exact counts, and each token's chosen expert is the unique
+    # maximum of its logits x W_r^T (computed exactly here in fp64)
+    counts = FFN_COUNTS + ZERO_COUNTS
+    x, w_r, bias, choice = inputs.counted_routing_inputs(counts, 128, "cpu", SEED)
+    assert np.array_equal(np.bincount(choice.numpy(), minlength=len(counts)), np.array(counts))
+    z = x.double() @ w_r.double().T + bias.double()
+    top2 = torch.topk(z, 2, dim=1)
+    assert torch.equal(top2.indices[:, 0], choice)
+    assert bool((top2.values[:, 0] - top2.values[:, 1] > 0.5).all())
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("wdtype", ["fp8", "fp8a8"])
 def test_forward_fp8_at_row_count_boundaries(wdtype):
