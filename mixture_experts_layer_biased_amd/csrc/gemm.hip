@@ -581,45 +581,76 @@ __global__ __launch_bounds__(512) void gemm_big_dma_kernel(GemmArgs a) {
     // this lane (a = gate pre-activation, c = up): h = silu(a) c; dh = g Q;
     // dU = [dh c silu'(a); dh silu(a)]; g h; and <Q, h> over the lane's
     // columns, summed with the other lane of the row: one partial per row,
-    // slice and wave (32 columns).
+    // slice and wave (32 columns). Q comes in, and dU and g h go out, through
+    // this wave's 10 KB of LDS (the ring is free after the barrier): Q as
+    // whole 128-byte row segments (8 rows per load, chunk c of row r at
+    // c ^ (r & 7)), the outputs as 64-byte row segments (16 rows per store,
+    // chunk c of row r at c ^ ((r >> 2) & 3)).
+    raw_barrier();
     const int pcount = 4 * a.nslices;
+    uint4* sq = lds + wave * 640;  // Q: 32 rows x 8 chunks
+    uint4* so = sq + 256;          // dU gate, dU up, g h: 3 x 32 rows x 4 chunks
+    const int col0 = slice * kBigColsGateUp + 32 * wn;
+    auto sw4 = [](int r) { return (r >> 2) & 3; };
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       if (frow(i) >= rows) continue;
-      const int r = frow(i) + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 8 * j + lane / 8, c = lane % 8;
+        const int tr = frow(i) + rr, col = col0 + 4 * c;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tr < rows && col < a.n_out)
+          v = *reinterpret_cast<const uint4*>(a.bq + (size_t)(rowbase + tr) * a.n_out + col);
+        sq[rr * 8 + (c ^ (rr & 7))] = v;
+      }
+      const int lr = lane & 31;
+      const int r = frow(i) + lr;
       const bool ok = r < rows;
       const size_t srow = (size_t)rowbase + (ok ? r : 0);
       const float g = ok ? a.bgate[a.perm[srow]] : 0.f;
       float part = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = slice * kBigColsGateUp + 32 * wn + 8 * q + 4 * h;
-        if (ok && j < a.n_out) {
-          const float4 qv = *reinterpret_cast<const float4*>(a.bq + srow * a.n_out + j);
-          const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
-          float da[4], dc[4], hg[4];
+        const int j = col0 + 8 * q + 4 * h;
+        const uint4 qw = sq[lr * 8 + ((2 * q + h) ^ (lr & 7))];
+        const float qa[4] = {__uint_as_float(qw.x), __uint_as_float(qw.y), __uint_as_float(qw.z),
+                             __uint_as_float(qw.w)};
+        float da[4], dc[4], hg[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float av = acc[i][0][4 * q + u], cv = acc[i][1][4 * q + u];
-            const float sg = 1.0f / (1.0f + expf(-av));
-            const float si = av * sg;
-            const float hv = si * cv;
-            part += qa[u] * hv;
-            const float dh = g * qa[u];
-            da[u] = dh * cv * (sg * (1.0f + av * (1.0f - sg)));
-            dc[u] = dh * si;
-            hg[u] = g * hv;
-          }
-          uint16_t* du = a.bdu + srow * 2 * a.n_out;
-          *reinterpret_cast<uint2*>(du + j) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
-          *reinterpret_cast<uint2*>(du + a.n_out + j) =
-              make_uint2(pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3]));
-          *reinterpret_cast<uint2*>(a.out + srow * a.n_out + j) =
-              make_uint2(pack_bf16x2(hg[0], hg[1]), pack_bf16x2(hg[2], hg[3]));
+        for (int u = 0; u < 4; ++u) {
+          const float av = acc[i][0][4 * q + u], cv = acc[i][1][4 * q + u];
+          const float sg = 1.0f / (1.0f + expf(-av));
+          const float si = av * sg;
+          const float hv = si * cv;
+          if (ok && j < a.n_out) part += qa[u] * hv;
+          const float dh = g * qa[u];
+          da[u] = dh * cv * (sg * (1.0f + av * (1.0f - sg)));
+          dc[u] = dh * si;
+          hg[u] = g * hv;
         }
+        const int off = lr * 4 + (q ^ sw4(lr));
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(so + off) + 8 * h) =
+            make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(so + 128 + off) + 8 * h) =
+            make_uint2(pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(so + 256 + off) + 8 * h) =
+            make_uint2(pack_bf16x2(hg[0], hg[1]), pack_bf16x2(hg[2], hg[3]));
       }
       part += __shfl_xor(part, 32, kWave);
       if (ok && h == 0) a.bdgp[srow * pcount + 4 * slice + wn] = part;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rr = 16 * j + lane / 4, c = lane % 4;
+        const int tr = frow(i) + rr, col = col0 + 8 * c;
+        if (tr < rows && col < a.n_out) {
+          const size_t orow = (size_t)rowbase + tr;
+          const int off = rr * 4 + (c ^ sw4(rr));
+          *reinterpret_cast<uint4*>(a.bdu + orow * 2 * a.n_out + col) = so[off];
+          *reinterpret_cast<uint4*>(a.bdu + orow * 2 * a.n_out + a.n_out + col) = so[128 + off];
+          *reinterpret_cast<uint4*>(a.out + orow * a.n_out + col) = so[256 + off];
+        }
+      }
     }
     return;
   }
