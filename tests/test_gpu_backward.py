@@ -97,6 +97,8 @@ def test_backward_odd_multiples_of_32(d, inter, T):
 
 @pytest.mark.parametrize("kw,T", [
     (dict(d=128, n_ffn=1, n_zero=0, k=1, inter=64), 100),      # one FFN expert: dz = 0
+    (dict(d=128, n_ffn=1, n_zero=0, k=1, inter=64), 1000),     # every token on it: four 256-row
+                                                                # dgrad tiles, a 16-stage wgrad k
     (dict(n_ffn=8, n_zero=4, k=12), 50),                        # K = E: a dense mixture
     (dict(n_ffn=1536, n_zero=512, k=64, inter=32), 64),          # the largest E and K accepted
 ])
