@@ -1,5 +1,7 @@
 // Weighted combine with the zero-computation-expert identity, and the
 // expert-bias update.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -80,6 +82,31 @@ __global__ __launch_bounds__(256) void bias_update_kernel(const int* __restrict_
   const double num = k_e * (double)t_all - (double)N * (double)counts[i];
   const double delta = (mu * num) / den;
   bias[i] = (float)((double)bias[i] + delta);
+}
+
+// Zero fill of a caller buffer (outputs of calls with no tokens). A kernel
+// rather than a memset node, so every entry point enqueues kernels only and
+// can be captured into a HIP graph. Words before the first 16-byte boundary
+// and after the last are written one at a time, the rest 16 bytes at a time.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* __restrict__ p, size_t head,
+                                                        size_t nvec, size_t tail) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  if (i < head) p[i] = 0u;
+  uint4* v = reinterpret_cast<uint4*>(p + head);
+  for (size_t j = i; j < nvec; j += stride) v[j] = make_uint4(0u, 0u, 0u, 0u);
+  if (i < tail) p[head + 4 * nvec + i] = 0u;
+}
+
+void launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return;
+  const size_t mis = ((uintptr_t)p & 15u) / 4;  // p is 4-byte aligned
+  const size_t head = std::min(words, mis ? 4 - mis : 0);
+  const size_t nvec = (words - head) / 4;
+  const size_t tail = words - head - 4 * nvec;
+  const size_t blocks = std::max<size_t>(1, std::min<size_t>(8192, (nvec + 255) / 256));
+  zero_fill_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), head, nvec, tail);
 }
 
 void launch_combine(const uint16_t* x, const uint16_t* Y, const int* /*idx*/, const float* gate,

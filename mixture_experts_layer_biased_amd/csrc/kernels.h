@@ -75,6 +75,8 @@ void launch_quant_rows(const uint16_t* src, int rows, const int* rows_dev, int c
                        float* scale, uint16_t* deq, int grid, hipStream_t s);
 void launch_combine(const uint16_t* x, const uint16_t* Y, const int* idx, const float* gate,
                     const int* row_of_slot, int T, int d, int K, uint16_t* y, hipStream_t s);
+// Zero bytes [p, p + bytes) of a 4-byte aligned buffer (bytes % 4 == 0).
+void launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, double k_e,
                         float* bias, hipStream_t s);
 

@@ -144,6 +144,26 @@ BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
   return B;
 }
 
+// Largest layout over every T <= tmax, so a workspace sized for tmax serves
+// any smaller call and the size is non-decreasing in tmax. Every region
+// grows with T except the router's split-K partials, whose split factor
+// depends on T only through ceil(T / 256) and falls as T grows: within each
+// run of 256 token counts the layout grows with T, so its largest value is
+// at the run's last T. Once the split factor is 1 it stays 1 and the layout
+// only grows.
+template <typename F>
+size_t max_total_upto(const lcmoe_shape& s, int tmax, F total) {
+  size_t best = total(tmax);
+  const int E = (int)n_experts(s);
+  for (long long t = 256; t < tmax; t += 256) {
+    best = std::max(best, total((int)t));
+    int ks = 1, kchunk = 0;
+    router_splits((int)t, E, s.d_model, ks, kchunk);
+    if (ks == 1) break;
+  }
+  return best;
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Carve the workspace: returns the aligned base or nullptr if too small.
@@ -195,13 +215,8 @@ extern "C" {
 size_t lcmoe_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens) {
   if (check_shape(shape) != LCMOE_OK || max_tokens < 0) return 0;
   if ((long long)max_tokens * shape->top_k >= (1ll << 31)) return 0;
-  // The router split factor shrinks as T grows; take the maximum over all
-  // T <= max_tokens so the result is non-decreasing in max_tokens (splits
-  // are 1 beyond 32768 tokens, where the layout grows with T).
-  size_t best = make_layout(*shape, max_tokens).total;
-  const int lim = std::min<int>(max_tokens, 32768);
-  for (int t = 1; t <= lim; ++t) best = std::max(best, make_layout(*shape, t).total);
-  return best + kAlign;
+  const lcmoe_shape s = *shape;
+  return max_total_upto(s, max_tokens, [&](int t) { return make_layout(s, t).total; }) + kAlign;
 }
 
 lcmoe_status lcmoe_route(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
@@ -217,8 +232,9 @@ lcmoe_status lcmoe_route(const lcmoe_shape* shape, int32_t T, const void* x_bf16
   if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
   const int E = (int)n_experts(*shape);
   if (T == 0) {
-    if (hipMemsetAsync(counts, 0, (size_t)E * 4, stream) != hipSuccess) return LCMOE_ERR_HIP;
-    return LCMOE_OK;
+    clear_hip_error();
+    launch_zero_fill(counts, (size_t)E * 4, stream);
+    return hip_status();
   }
   if (!aligned16(x_bf16) || !aligned16(w_router)) return LCMOE_ERR_UNSUPPORTED;
   const Layout L = make_layout(*shape, T);
@@ -242,10 +258,10 @@ lcmoe_status lcmoe_permute(const lcmoe_shape* shape, int32_t T, const int32_t* t
   if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
   const int E = (int)n_experts(*shape);
   if (T == 0) {
-    if (hipMemsetAsync(counts, 0, (size_t)E * 4, stream) != hipSuccess ||
-        hipMemsetAsync(offsets, 0, (size_t)(shape->n_ffn + 1) * 4, stream) != hipSuccess)
-      return LCMOE_ERR_HIP;
-    return LCMOE_OK;
+    clear_hip_error();
+    launch_zero_fill(counts, (size_t)E * 4, stream);
+    launch_zero_fill(offsets, (size_t)(shape->n_ffn + 1) * 4, stream);
+    return hip_status();
   }
   const Layout L = make_layout(*shape, T);
   char* base = ws_base(ws, ws_bytes, L.routing_end);
@@ -282,9 +298,9 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   // x rows are gathered with 32-bit byte offsets.
   if ((long long)T * shape->d_model * 2 >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
   if (T == 0) {
-    if (hipMemsetAsync(counts, 0, (size_t)n_experts(*shape) * 4, stream) != hipSuccess)
-      return LCMOE_ERR_HIP;
-    return LCMOE_OK;
+    clear_hip_error();
+    launch_zero_fill(counts, (size_t)n_experts(*shape) * 4, stream);
+    return hip_status();
   }
   if (!aligned16(x_bf16) || !aligned16(w_router) || !aligned16(w13) || !aligned16(w2) ||
       !aligned16(y_bf16))
@@ -435,10 +451,9 @@ lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T, const void* x_bf
 size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens) {
   if (check_shape(shape) != LCMOE_OK || max_tokens < 0 || shape->w_dtype != LCMOE_W_BF16) return 0;
   if ((long long)max_tokens * shape->top_k >= (1ll << 31)) return 0;
-  size_t best = make_bwd_layout(*shape, max_tokens).total;
-  const int lim = std::min<int>(max_tokens, 32768);
-  for (int t = 1; t <= lim; ++t) best = std::max(best, make_bwd_layout(*shape, t).total);
-  return best + kAlign;
+  const lcmoe_shape s = *shape;
+  return max_total_upto(s, max_tokens, [&](int t) { return make_bwd_layout(s, t).total; }) +
+         kAlign;
 }
 
 namespace {
@@ -467,11 +482,11 @@ lcmoe_status backward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf
   if ((long long)T * std::max<long long>(std::max(d, 2 * I), 6 * Ep) * 2 >= (1ll << 32))
     return LCMOE_ERR_UNSUPPORTED;
   if (T == 0) {  // no tokens: every gradient is zero
-    if (hipMemsetAsync(dw_router, 0, (size_t)E * d * 4, stream) != hipSuccess ||
-        hipMemsetAsync(dw13, 0, (size_t)N * 2 * I * d * 2, stream) != hipSuccess ||
-        hipMemsetAsync(dw2, 0, (size_t)N * d * I * 2, stream) != hipSuccess)
-      return LCMOE_ERR_HIP;
-    return LCMOE_OK;
+    clear_hip_error();
+    launch_zero_fill(dw_router, (size_t)E * d * 4, stream);
+    launch_zero_fill(dw13, (size_t)N * 2 * I * d * 2, stream);
+    launch_zero_fill(dw2, (size_t)N * d * I * 2, stream);
+    return hip_status();
   }
   if (!aligned16(x_bf16) || !aligned16(w_router) || !aligned16(w13) || !aligned16(w2) ||
       !aligned16(dy_bf16) || !aligned16(dx) || !aligned16(dw_router) || !aligned16(dw13) ||

@@ -146,6 +146,34 @@ def test_workspace_monotone(dims):
     assert lcmoe.workspace_bytes(s, 8192) >= 8192 * min(K, N) * (I + d) * 2
 
 
+@pytest.mark.parametrize("dims", [(64, 8, 4, 3, 32), (1024, 64, 32, 6, 512), (512, 100, 28, 4, 64)])
+def test_workspace_monotone_past_32k_tokens(dims):
+    # With few experts (E <= 128) the router still splits its k range beyond
+    # 32768 tokens; the size must stay non-decreasing there, forward and
+    # backward, at every run boundary of 256 tokens and around it.
+    s = make_shape(*dims)
+    Ts = sorted({t for j in range(127, 520, 7) for t in (256 * j - 1, 256 * j, 256 * j + 1)}
+                | {32767, 32768, 32769, 65535, 65536, 65537, 131073})
+    prev_f = prev_b = 0
+    for T in Ts:
+        f, b = lcmoe.workspace_bytes(s, T), lcmoe.backward_workspace_bytes(s, T)
+        assert f >= prev_f and b >= prev_b, (T, f, prev_f, b, prev_b)
+        prev_f, prev_b = f, b
+
+
+def test_zero_tokens_validation():
+    # T = 0 still validates its arguments before anything is enqueued
+    s = shp()
+    assert _route(s, 0, c=None) == ERR_INVALID_ARG
+    assert _forward(s, 0, c=None) == ERR_INVALID_ARG
+    assert _forward(shp(w_dtype=1), 0) == ERR_UNSUPPORTED
+    L = lcmoe.lib()
+    assert L.lcmoe_permute(ctypes.byref(s), 0, FAKE, None, FAKE, FAKE, FAKE, None, 0,
+                           None) == ERR_INVALID_ARG
+    assert _backward(s, 0, dw13=None) == ERR_INVALID_ARG
+    assert lcmoe.workspace_bytes(s, 0) > 0
+
+
 def _stats(shape, T, x=FAKE, lg=FAKE, c=FAKE, D=2, k_e=2.0, alpha=1.0, lam=1.0, st=FAKE, ws=None,
            wsb=0):
     L = lcmoe.lib()
