@@ -22,6 +22,8 @@ from .lcmoe_oracle import (  # noqa: F401
     dequant_rows_fp8,
     round_to_bf16,
     expert_ffn_a8,
+    expert_gate_up,
+    expert_down_fp8_rows,
     router_logits,
     selection_scores,
     select_topk,
@@ -31,6 +33,7 @@ from .lcmoe_oracle import (  # noqa: F401
     silu,
     expert_ffn,
     combine_given_routing,
+    combine_given_expert_outputs,
     route,
     forward,
     dense_masked_forward,

@@ -253,19 +253,37 @@ def silu(u):
         return u / (1.0 + np.exp(-u))
 
 
+def expert_gate_up(x_rows, w13):
+    """First half of the SiLU-gated FFN expert (reading R-ffn): the
+    intermediate h = silu(x W1^T) * (x W3^T), fp64, not rounded.
+
+    x_rows: [m, d]; w13: [2I, d] with gate rows [0, I) and up rows [I, 2I).
+    Returns [m, I].
+    """
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    w13 = np.asarray(w13, dtype=np.float64)
+    inter = w13.shape[0] // 2
+    u = x_rows @ w13.T
+    return silu(u[:, :inter]) * u[:, inter:]
+
+
 def expert_ffn(x_rows, w13, w2):
     """SiLU-gated FFN expert (reading R-ffn).
 
     x_rows: [m, d]; w13: [2I, d] with gate rows [0, I) and up rows [I, 2I);
     w2: [d, I]. Returns [m, d] = (silu(x W1^T) * (x W3^T)) W2^T in fp64.
     """
-    x_rows = np.asarray(x_rows, dtype=np.float64)
-    w13 = np.asarray(w13, dtype=np.float64)
     w2 = np.asarray(w2, dtype=np.float64)
-    inter = w2.shape[1]
-    u = x_rows @ w13.T
-    h = silu(u[:, :inter]) * u[:, inter:]
-    return h @ w2.T
+    return expert_gate_up(x_rows, w13) @ w2.T
+
+
+def expert_down_fp8_rows(h_codes, h_scales, w2):
+    """Second half of the expert with fp8 activations (reading R-a8): the
+    intermediate given as per-row E4M3FN codes and fp32 row scales, its value
+    q * s (exact in fp64) times W2^T. h_codes: uint8 [m, I]; h_scales: [m];
+    w2: [d, I]. Returns [m, d], fp64."""
+    w2 = np.asarray(w2, dtype=np.float64)
+    return dequant_rows_fp8(h_codes, h_scales) @ w2.T
 
 
 def expert_ffn_a8(x_hat_rows, w13, w2):
@@ -273,14 +291,9 @@ def expert_ffn_a8(x_hat_rows, w13, w2):
     x_hat_rows are already quantized-dequantized; the intermediate
     h = silu(x W1^T) * (x W3^T) is rounded to bf16, quantized per row, and
     its dequantized value multiplies W2^T. fp64 otherwise."""
-    x_hat_rows = np.asarray(x_hat_rows, dtype=np.float64)
-    w13 = np.asarray(w13, dtype=np.float64)
-    w2 = np.asarray(w2, dtype=np.float64)
-    inter = w2.shape[1]
-    u = x_hat_rows @ w13.T
-    h = round_to_bf16(silu(u[:, :inter]) * u[:, inter:])
+    h = round_to_bf16(expert_gate_up(x_hat_rows, w13))
     hq, hs = quantize_rows_fp8(h.astype(np.float32))
-    return dequant_rows_fp8(hq, hs) @ w2.T
+    return expert_down_fp8_rows(hq, hs, w2)
 
 
 def combine_given_routing(x, idx, g, n_ffn, get_expert, tokens=None, a8=False):
@@ -318,6 +331,23 @@ def combine_given_routing(x, idx, g, n_ffn, get_expert, tokens=None, a8=False):
             out = expert_ffn(x_ffn[rows], w13_e, w2_e)
         y[rows] += sub_g[rows, ks][:, None] * out
     return y
+
+
+def combine_given_expert_outputs(x, idx, g, n_ffn, ffn_out):
+    """The MoE sum of section 2.1 with each FFN slot's expert output given:
+    y_t = sum_k g[t,k] * (ffn_out[t,k] if idx[t,k] < N else x_t), fp64.
+
+    x: [T, d]; idx, g: [T, K]; ffn_out: [T, K, d] (rows of zero-expert slots
+    are not read). Used where the expert outputs come from given
+    intermediates (the fp8-activation expert's down half on given codes).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    g = np.asarray(g, dtype=np.float64)
+    ffn_out = np.asarray(ffn_out, dtype=np.float64)
+    ffn = idx < n_ffn
+    v = np.where(ffn[:, :, None], ffn_out, x[:, None, :])
+    return (g[:, :, None] * v).sum(axis=1)
 
 
 def route(x, w_router, bias, k):

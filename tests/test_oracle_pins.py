@@ -571,6 +571,55 @@ def test_a8_expert_matches_torch_composition():
     assert 1e-4 < rel < 0.1
 
 
+def test_expert_halves_match_torch():
+    # The two halves of the expert against torch primitives: silu gate times
+    # up (gate rows first; swapping the halves or transposing W13 changes the
+    # result), and the down half on given per-row fp8 codes (torch's
+    # float8_e4m3fn decode times the row scale, then W2^T).
+    rng = np.random.default_rng(4)
+    d, inter, m = 192, 96, 7
+    x = rng.normal(size=(m, d))
+    w13 = rng.normal(size=(2 * inter, d)) * 0.05
+    w2 = rng.normal(size=(d, inter)) * 0.05
+    X, W13 = torch.tensor(x), torch.tensor(w13)
+    want_h = (torch.nn.functional.silu(X @ W13[:inter].T) * (X @ W13[inter:].T)).numpy()
+    got_h = oracle.expert_gate_up(x, w13)
+    assert np.allclose(got_h, want_h, rtol=1e-13, atol=1e-13 * np.abs(want_h).max())
+    swapped = (torch.nn.functional.silu(X @ W13[inter:].T) * (X @ W13[:inter].T)).numpy()
+    assert np.abs(got_h - swapped).max() > 1e-2 * np.abs(want_h).max()
+    assert np.allclose(oracle.expert_ffn(x, w13, w2), want_h @ w2.T, rtol=1e-12,
+                       atol=1e-12 * np.abs(want_h @ w2.T).max())
+    codes = rng.integers(0, 256, size=(m, inter), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11            # no NaN codes
+    scales = np.exp(rng.uniform(-8, 2, m)).astype(np.float32)
+    q = torch.tensor(codes).view(torch.float8_e4m3fn).double()
+    want_y = ((q * torch.tensor(scales).double()[:, None]) @ torch.tensor(w2).T).numpy()
+    got_y = oracle.expert_down_fp8_rows(codes, scales, w2)
+    assert np.allclose(got_y, want_y, rtol=1e-13, atol=1e-13 * np.abs(want_y).max())
+
+
+def test_combine_given_expert_outputs_matches_sparse_combine():
+    # The MoE sum over given per-slot expert outputs equals the sparse combine
+    # that evaluates the experts itself, on the small config's routing (FFN
+    # and zero slots mixed, several slots of a token on one expert group).
+    cfg = inputs.CONFIGS["small"]
+    L = inputs.make_layer(cfg, "cpu")
+    x = bf16_values(inputs.make_tokens(cfg, "cpu", tokens=48))
+    r = oracle.route(x, L["w_router"].numpy(), L["bias"].numpy(), cfg.k)
+    get = expert_getter(L, cfg)
+    want = oracle.combine_given_routing(x, r["idx"], r["g"], cfg.n_ffn, get)
+    out = np.full((x.shape[0], cfg.k, cfg.d), np.nan)  # zero-expert rows must not be read
+    for t in range(x.shape[0]):
+        for k in range(cfg.k):
+            e = int(r["idx"][t, k])
+            if e < cfg.n_ffn:
+                w13, w2 = get(e)
+                out[t, k] = oracle.expert_ffn(x[t:t + 1], w13, w2)[0]
+    assert (r["idx"] >= cfg.n_ffn).any() and (r["idx"] < cfg.n_ffn).any()
+    got = oracle.combine_given_expert_outputs(x, r["idx"], r["g"], cfg.n_ffn, out)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
 def test_a8_zero_routing_is_exact_identity():
     # FFN experts biased out: y = (sum_k g) x exactly, the identity sees exact x.
     cfg = inputs.CONFIGS["tiny"]
