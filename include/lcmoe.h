@@ -168,6 +168,37 @@ lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T,
                            int32_t* topk_idx, float* topk_gate, int32_t* counts,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* lcmoe_forward for fp8 weights and fp8 activations (LCMOE_W_FP8_E4M3_B128_A8)
+ * that also hands the activation path's intermediates to the caller, for
+ * verification harnesses: the same kernels on the same values (every output
+ * of lcmoe_forward bit for bit), with the quantized token rows and the FFN
+ * intermediate written to these caller buffers instead of the workspace.
+ * The per-row quantization is the reading stated at LCMOE_W_FP8_E4M3_B128_A8
+ * (the pages name FP8 quantization, "LongCat-Flash" section 5, without the
+ * activation scheme).
+ *
+ *   xq  [T][d]  uint8 out: E4M3FN codes of every token row x_t
+ *   xs  [T]     fp32 out: the row scales s = fl32(amax / 448)
+ *   h   [S][I]  bf16 out: H = silu(x W1^T) * (x W3^T) of every FFN slot row,
+ *               before its quantization
+ *   hq  [S][I]  uint8 out: E4M3FN codes of H
+ *   hs  [S]     fp32 out: the row scales of H
+ * with S = T * min(K, N) rows allocated; row r is FFN slot row r of the
+ * expert-grouped slot order (lcmoe_permute's perm: grouped by expert, slot id
+ * ascending inside a group) and rows at or past the FFN slot count are not
+ * written. Other arguments, errors and outputs as lcmoe_forward; also
+ * UNSUPPORTED for another weight type or a buffer not 16-byte aligned, and
+ * INVALID_ARG for a null buffer with T > 0. The buffers are caller-owned
+ * device memory and must not overlap the workspace. */
+lcmoe_status lcmoe_forward_inspect(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias,
+                                   const void* w13, const float* w13_scale,
+                                   const void* w2, const float* w2_scale,
+                                   void* y_bf16,
+                                   int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                                   void* xq, float* xs, void* h, void* hq, float* hs,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Stages of lcmoe_forward, in launch order (for lcmoe_forward_staged). */
 typedef enum {
   LCMOE_STAGE_ROUTER = 0,     /* router logits                          */

@@ -276,18 +276,16 @@ lcmoe_status lcmoe_permute(const lcmoe_shape* shape, int32_t T, const int32_t* t
 
 namespace {
 
-// The forward; usave (bf16 weights only, may be null) receives the gate/up
-// pre-activations of every FFN slot row.
-lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
-                          const float* w_router, const float* bias, const void* w13,
-                          const float* w13_scale, const void* w2, const float* w2_scale,
-                          void* y_bf16, int32_t* topk_idx, float* topk_gate, int32_t* counts,
-                          void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events,
-                          float* usave) {
+// Argument checks of the forward entry points (everything but the
+// workspace), before any HIP call.
+lcmoe_status check_forward_args(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                const float* w_router, const float* bias, const void* w13,
+                                const float* w13_scale, const void* w2, const float* w2_scale,
+                                const void* y_bf16, const int32_t* topk_idx,
+                                const float* topk_gate, const int32_t* counts) {
   lcmoe_status st = check_shape(shape);
   if (st != LCMOE_OK) return st;
-  const bool fp8 = shape->w_dtype != LCMOE_W_BF16;          // fp8 weights
-  const bool a8 = shape->w_dtype == LCMOE_W_FP8_E4M3_B128_A8;  // and fp8 activations
+  const bool fp8 = shape->w_dtype != LCMOE_W_BF16;  // fp8 weights
   if (T < 0 || counts == nullptr) return LCMOE_ERR_INVALID_ARG;
   if (T > 0 && (x_bf16 == nullptr || w_router == nullptr || bias == nullptr || w13 == nullptr ||
                 w2 == nullptr || y_bf16 == nullptr || topk_idx == nullptr ||
@@ -297,14 +295,41 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   if ((long long)T * shape->top_k >= (1ll << 31)) return LCMOE_ERR_UNSUPPORTED;
   // x rows are gathered with 32-bit byte offsets.
   if ((long long)T * shape->d_model * 2 >= (1ll << 32)) return LCMOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!aligned16(x_bf16) || !aligned16(w_router) || !aligned16(w13) ||
+                !aligned16(w2) || !aligned16(y_bf16)))
+    return LCMOE_ERR_UNSUPPORTED;
+  return LCMOE_OK;
+}
+
+// Caller buffers that receive the fp8 activation path's intermediates in
+// place of the workspace regions (lcmoe_forward_inspect).
+struct A8Out {
+  uint8_t* xq = nullptr;
+  float* xs = nullptr;
+  uint16_t* h = nullptr;
+  uint8_t* hq = nullptr;
+  float* hs = nullptr;
+};
+
+// The forward; usave (bf16 weights only, may be null) receives the gate/up
+// pre-activations of every FFN slot row; a8o (fp8 activations only, may be
+// null) redirects the activation codes, scales and the pre-quantization H.
+lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                          const float* w_router, const float* bias, const void* w13,
+                          const float* w13_scale, const void* w2, const float* w2_scale,
+                          void* y_bf16, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                          void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events,
+                          float* usave, const A8Out* a8o = nullptr) {
+  lcmoe_status st = check_forward_args(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2,
+                                       w2_scale, y_bf16, topk_idx, topk_gate, counts);
+  if (st != LCMOE_OK) return st;
+  const bool fp8 = shape->w_dtype != LCMOE_W_BF16;             // fp8 weights
+  const bool a8 = shape->w_dtype == LCMOE_W_FP8_E4M3_B128_A8;  // and fp8 activations
   if (T == 0) {
     clear_hip_error();
     launch_zero_fill(counts, (size_t)n_experts(*shape) * 4, stream);
     return hip_status();
   }
-  if (!aligned16(x_bf16) || !aligned16(w_router) || !aligned16(w13) || !aligned16(w2) ||
-      !aligned16(y_bf16))
-    return LCMOE_ERR_UNSUPPORTED;
   const Layout L = make_layout(*shape, T);
   char* base = ws_base(ws, ws_bytes, L.total);
   if (base == nullptr) return LCMOE_ERR_WORKSPACE;
@@ -315,6 +340,21 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   int* row_of_slot = at<int>(base, L.row_of_slot);
   const int E = (int)n_experts(*shape);
   hipEvent_t* ev = stage_events;
+  // fp8 activations: codes and scales of x and of H, and H before its
+  // quantization (the workspace, or the caller's buffers when inspected)
+  uint8_t* xq = a8 ? at<uint8_t>(base, L.xq) : nullptr;
+  float* xs = a8 ? at<float>(base, L.xs) : nullptr;
+  uint8_t* hq = a8 ? at<uint8_t>(base, L.hq) : nullptr;
+  float* hs = a8 ? at<float>(base, L.hs) : nullptr;
+  uint16_t* H = at<uint16_t>(base, L.H);
+  uint16_t* Hpre = H;  // quantized in place unless inspected
+  if (a8o != nullptr) {
+    xq = a8o->xq;
+    xs = a8o->xs;
+    hq = a8o->hq;
+    hs = a8o->hs;
+    Hpre = a8o->h;
+  }
   mark(ev, 0, stream);
   {
     float* zpart = at<float>(base, L.zpart);
@@ -328,14 +368,12 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
                    at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.small_list),
                    at<int>(base, L.mt_prefix), at<int>(base, L.meta), perm, row_of_slot, stream);
     if (a8)  // fp8 activations: quantize x per row (timed with the permutation stage)
-      launch_quant_rows(static_cast<const uint16_t*>(x_bf16), T, nullptr, shape->d_model,
-                        at<uint8_t>(base, L.xq), at<float>(base, L.xs),
+      launch_quant_rows(static_cast<const uint16_t*>(x_bf16), T, nullptr, shape->d_model, xq, xs,
                         at<uint16_t>(base, L.xdeq), std::min(2048, (T + 3) / 4), stream);
     mark(ev, 3, stream);
   }
 
   const int N = shape->n_ffn, d = shape->d_model, I = shape->d_expert;
-  uint16_t* H = at<uint16_t>(base, L.H);
   uint16_t* Y = at<uint16_t>(base, L.Y);
 
   // Grid bounds from what the host knows (no device->host sync): at most
@@ -368,9 +406,9 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   // The small-M path reads bf16 activations: with fp8 activations, the
   // dequantized rows fl32(q) * s rounded to bf16.
   a.src = a8 ? at<uint16_t>(base, L.xdeq) : static_cast<const uint16_t*>(x_bf16);
-  a.src8 = a8 ? at<uint8_t>(base, L.xq) : nullptr;
-  a.ascale = a8 ? at<float>(base, L.xs) : nullptr;
-  a.out = H;
+  a.src8 = xq;
+  a.ascale = xs;
+  a.out = Hpre;
   a.usave = usave;
   a.kdim = d;
   a.n_out = I;
@@ -382,18 +420,17 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   if (a8) launch_gemm_big_a8(a, true, big_grid(a.nslices), stream);
   else launch_gemm_big(a, true, fp8, big_grid(a.nslices), stream);
   mark(ev, 5, stream);
-  if (a8)  // quantize the S rows of H (S read on the device), dequantized copy in place
-    launch_quant_rows(H, 0, at<int>(base, L.meta) + 2, I, at<uint8_t>(base, L.hq),
-                      at<float>(base, L.hs), H, (int)std::min<long long>(2048, (smax + 3) / 4),
-                      stream);
+  if (a8)  // quantize the S rows of H (S read on the device); dequantized bf16 copy into H
+    launch_quant_rows(Hpre, 0, at<int>(base, L.meta) + 2, I, hq, hs, H,
+                      (int)std::min<long long>(2048, (smax + 3) / 4), stream);
 
   // down: Y = H W2^T
   a.usave = nullptr;
   a.w = w2;
   a.wscale = w2_scale;
   a.src = H;
-  a.src8 = a8 ? at<uint8_t>(base, L.hq) : nullptr;
-  a.ascale = a8 ? at<float>(base, L.hs) : nullptr;
+  a.src8 = hq;
+  a.ascale = hs;
   a.out = Y;
   a.kdim = I;
   a.n_out = d;
@@ -446,6 +483,30 @@ lcmoe_status lcmoe_forward(const lcmoe_shape* shape, int32_t T, const void* x_bf
                            void* ws, size_t ws_bytes, hipStream_t stream) {
   return lcmoe_forward_staged(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale,
                               y_bf16, topk_idx, topk_gate, counts, ws, ws_bytes, stream, nullptr);
+}
+
+lcmoe_status lcmoe_forward_inspect(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias, const void* w13,
+                                   const float* w13_scale, const void* w2, const float* w2_scale,
+                                   void* y_bf16, int32_t* topk_idx, float* topk_gate,
+                                   int32_t* counts, void* xq, float* xs, void* h, void* hq,
+                                   float* hs, void* ws, size_t ws_bytes, hipStream_t stream) {
+  lcmoe_status st = check_shape(shape);
+  if (st != LCMOE_OK) return st;
+  if (shape->w_dtype != LCMOE_W_FP8_E4M3_B128_A8) return LCMOE_ERR_UNSUPPORTED;
+  if (T > 0 && (xq == nullptr || xs == nullptr || h == nullptr || hq == nullptr || hs == nullptr))
+    return LCMOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(xq) || !aligned16(xs) || !aligned16(h) || !aligned16(hq) ||
+                !aligned16(hs)))
+    return LCMOE_ERR_UNSUPPORTED;
+  A8Out o;
+  o.xq = static_cast<uint8_t*>(xq);
+  o.xs = xs;
+  o.h = static_cast<uint16_t*>(h);
+  o.hq = static_cast<uint8_t*>(hq);
+  o.hs = hs;
+  return forward_impl(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale, y_bf16,
+                      topk_idx, topk_gate, counts, ws, ws_bytes, stream, nullptr, nullptr, &o);
 }
 
 size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens) {

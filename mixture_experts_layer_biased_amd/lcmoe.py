@@ -17,7 +17,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 W_BF16, W_FP8_E4M3_B128, W_FP8_E4M3_B128_A8 = 0, 1, 2
 
 EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
-           "lcmoe_forward_staged", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
+           "lcmoe_forward_staged", "lcmoe_forward_inspect", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
            "lcmoe_router_stats", "lcmoe_backward_workspace_bytes", "lcmoe_backward",
            "lcmoe_backward_staged", "lcmoe_forward_train", "lcmoe_backward_saved",
            "lcmoe_status_str")
@@ -79,6 +79,8 @@ def lib():
     L.lcmoe_forward_staged.argtypes = [S, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        sz, _P, _P]
     L.lcmoe_forward_staged.restype = st
+    L.lcmoe_forward_inspect.argtypes = [S, i32] + [_P] * 17 + [sz, _P]
+    L.lcmoe_forward_inspect.restype = st
     L.lcmoe_bias_update.argtypes = [S, i32, _P, ctypes.c_double, ctypes.c_double, _P, _P]
     L.lcmoe_bias_update.restype = st
     L.lcmoe_router_stats_workspace_bytes.argtypes = [S, i32]
@@ -261,6 +263,39 @@ def forward(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, ws
     else:
         _check(lib().lcmoe_forward_staged(*args, stage_events), "lcmoe_forward_staged")
     return dict(y=y, idx=idx, gate=gate, counts=counts)
+
+
+def forward_inspect(shape, x, w_router, bias, w13, w2, w13_scale, w2_scale, ws=None):
+    """lcmoe_forward_inspect (fp8 weights and activations): the forward's
+    outputs plus its fp8 activation intermediates. Returns dict(y, idx, gate,
+    counts, xq uint8 [T,d], xs fp32 [T], h bf16 [S,I], hq uint8 [S,I],
+    hs fp32 [S]) with S = u_rows(shape, T) rows allocated (rows at or past
+    the FFN slot count are left unwritten)."""
+    T = x.shape[0]
+    dev = x.device
+    K, E, d, I = shape.top_k, shape.n_experts, shape.d_model, shape.d_expert
+    _expect_layer(shape, T, x, w_router, bias)
+    _expect_experts(shape, w13, w2, w13_scale, w2_scale)
+    S = u_rows(shape, T)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    gate = torch.empty(T, K, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    xq = torch.empty(T, d, dtype=torch.uint8, device=dev)
+    xs = torch.empty(T, dtype=torch.float32, device=dev)
+    h = torch.empty(S, I, dtype=torch.bfloat16, device=dev)
+    hq = torch.empty(S, I, dtype=torch.uint8, device=dev)
+    hs = torch.empty(S, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev)
+    _dev(x, w_router, bias, w13, w2, w13_scale, w2_scale, y, idx, gate, counts, xq, xs, h, hq, hs,
+         ws)
+    _check(lib().lcmoe_forward_inspect(ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                       _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                       _ptr(y), _ptr(idx), _ptr(gate), _ptr(counts), _ptr(xq),
+                                       _ptr(xs), _ptr(h), _ptr(hq), _ptr(hs), _ptr(ws), ws.numel(),
+                                       _stream()), "lcmoe_forward_inspect")
+    return dict(y=y, idx=idx, gate=gate, counts=counts, xq=xq, xs=xs, h=h, hq=hq, hs=hs)
 
 
 def bias_update(shape, counts, mu, k_e, bias, t_all):

@@ -42,8 +42,93 @@ def oracle_forward_rows(cfg, L, x, idx_gpu, tokens, cache=None):
     z = oracle.router_logits(xv, L["w_router"].cpu().numpy())
     idx = idx_gpu[tokens]
     g, _ = oracle.softmax_gates(z, idx)
-    get = expert_getter(L, cfg.wdtype, cache=cache)
+    experts = np.unique(idx[idx < cfg.n_ffn])  # the oracle's combine visits them in this order
+    get = expert_getter(L, cfg.wdtype, cache=cache, prefetch=None if cache is not None else experts)
     return oracle.combine_given_routing(xv, idx, g, cfg.n_ffn, get, a8=cfg.wdtype == "fp8a8")
+
+
+def cover_tokens(idx, n_ffn, extra=()):
+    """Tokens whose selections together touch every FFN expert that any
+    token selected: for each touched expert in id order not yet covered,
+    its first token. Returns (sorted tokens including `extra`, number of
+    touched FFN experts, number covered)."""
+    idx = np.asarray(idx)
+    touched = np.unique(idx[idx < n_ffn])
+    covered = set()
+    toks = set(int(t) for t in extra)
+    for t in toks:
+        covered.update(int(e) for e in idx[t] if e < n_ffn)
+    for e in touched:
+        if int(e) in covered:
+            continue
+        t = int(np.flatnonzero((idx == e).any(axis=1))[0])
+        toks.add(t)
+        covered.update(int(v) for v in idx[t] if v < n_ffn)
+    return np.array(sorted(toks)), len(touched), len(covered & set(int(e) for e in touched))
+
+
+def check_fp8a8_chain(cfg, L, x, res, tokens, tol_h=2e-2, tol_y=5e-2):
+    """Stage-by-stage parity of the fp8-activation forward on `tokens`, from
+    lcmoe_forward_inspect's intermediates (res), each stage checked on the
+    GPU's own inputs to it so that an fp8 rounding flip upstream cannot
+    consume the tolerance downstream:
+      x codes and scales == the oracle's per-row quantizer, bit for bit;
+      H (before quantization) vs the oracle's gate/up half on the GPU's x
+        codes (one bf16 rounding of fp32-accumulated exact products: tol_h);
+      H codes and scales == the oracle's quantizer on the GPU's H, bit for bit;
+      y vs the oracle's MoE sum with each FFN slot's down half evaluated on
+        the GPU's H codes (tol_y, the fp8 bar).
+    Returns (max relative error of H, of y, FFN slot rows checked)."""
+    tokens = np.asarray(sorted(set(int(t) for t in tokens)))
+    K, N = cfg.k, cfg.n_ffn
+    idx_all = res["idx"].cpu().numpy()
+    idx = idx_all[tokens]
+    xv = bf16_values(x[tokens])
+    tsel = torch.as_tensor(tokens, device=x.device)
+    # 1. token rows: codes and scales
+    xq_ref, xs_ref = oracle.quantize_rows_fp8(xv.astype(np.float32))
+    xq = res["xq"][tsel].cpu().numpy()
+    xs = res["xs"][tsel].cpu().numpy()
+    assert np.array_equal(xq, xq_ref), "x codes differ from the oracle's quantizer"
+    assert np.array_equal(xs.view(np.uint32), xs_ref.view(np.uint32)), "x scales differ"
+    # 2. the FFN slot rows of these tokens, in the expert-grouped slot order
+    _, _, row_of_slot = oracle.permutation(idx_all, N)
+    slots = (tokens[:, None] * K + np.arange(K)[None, :])
+    rows = row_of_slot[slots]                       # [n, K], -1 for zero slots
+    ffn = rows >= 0
+    assert np.array_equal(ffn, idx < N)
+    r_sel = torch.as_tensor(rows[ffn], device=x.device)
+    h = bf16_values(res["h"][r_sel])
+    hq = res["hq"][r_sel].cpu().numpy()
+    hs = res["hs"][r_sel].cpu().numpy()
+    # 3. H codes and scales: the oracle's quantizer on the GPU's own H
+    hq_ref, hs_ref = oracle.quantize_rows_fp8(h.astype(np.float32))
+    assert np.array_equal(hq, hq_ref), "H codes differ from the oracle's quantizer"
+    assert np.array_equal(hs.view(np.uint32), hs_ref.view(np.uint32)), "H scales differ"
+    # 4. per expert: gate/up half on the GPU's x codes, down half on its H codes
+    xhat = oracle.dequant_rows_fp8(xq, xs)
+    pos_t, pos_k = np.nonzero(ffn)                 # same order as rows[ffn]
+    exp_of = idx[pos_t, pos_k]
+    h_ref = np.zeros_like(h)
+    out = np.zeros((len(tokens), K, cfg.d))
+    experts = np.unique(exp_of)
+    get = expert_getter(L, cfg.wdtype, prefetch=experts)
+    for e in experts:
+        sel = np.flatnonzero(exp_of == e)
+        w13, w2 = get(e)
+        h_ref[sel] = oracle.expert_gate_up(xhat[pos_t[sel]], w13)
+        out[pos_t[sel], pos_k[sel]] = oracle.expert_down_fp8_rows(hq[sel], hs[sel], w2)
+    err_h = max_rel_err(h, h_ref) if len(h) else 0.0  # no FFN slot among these tokens
+    z = oracle.router_logits(xv, L["w_router"].cpu().numpy())
+    g, _ = oracle.softmax_gates(z, idx)
+    y_ref = oracle.combine_given_expert_outputs(xv, idx, g, N, out)
+    err_y = max_rel_err(bf16_values(res["y"][tsel]), y_ref)
+    print(f"{cfg.name} T={x.shape[0]} fp8 activations: {len(tokens)} tokens, {int(ffn.sum())} FFN "
+          f"slot rows over {len(experts)} experts; codes and scales bit-exact; H max rel err "
+          f"{err_h:.3e}, y max rel err {err_y:.3e}")
+    assert err_h < tol_h, err_h
+    assert err_y < tol_y, err_y
+    return err_h, err_y, int(ffn.sum())
 
 
 def router_error_scale(x_vals, w_router, d):

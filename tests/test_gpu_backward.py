@@ -130,6 +130,50 @@ def test_backward_zero_routing_closed_form():
     check_all(cfg, L2, x, dy, res, idx, cache={})
 
 
+def dw13_excess(xv, dyv, g, w13, w2, got, ref, tol=TOL):
+    """Largest |GPU - oracle| / allowance over the elements of one expert's
+    dW13 = sum over its slots of du x^T, where allowance = max(tol times the
+    reference row's infinity norm, the fp32 error envelope of the element).
+
+    A row of dW13 is tied to one entry of du per slot, du = [dh c silu'(a);
+    dh silu(a)], and where that entry is small by cancellation (silu' has a
+    root near a = -1.28; a, c or Q = W2^T dy near zero) the row's relative
+    error is that of fp32 sums evaluated next to a root, not of the kernel.
+    The envelope propagates, to first order, the GPU's documented arithmetic:
+    a, c and Q accumulate exact bf16 products in fp32 (within
+    (k/16 + 32) 2^-24 sum |products| for a reduction of length k, the bound
+    used for the router's fp32 sums), silu and silu' are evaluated in fp32
+    (a few ulps of their terms), du is rounded once to bf16 (2^-9, taken as
+    2^-8 with the fp32 products), and dW13 once to bf16 (2^-8).
+    With got=None, returns (envelope, tol bar) per element instead."""
+    xv, dyv, g = np.asarray(xv), np.asarray(dyv), np.asarray(g)
+    d = xv.shape[1]
+    inter = w2.shape[1]
+    u = xv @ w13.T
+    a, c = u[:, :inter], u[:, inter:]
+    Q = dyv @ w2
+    dh = g[:, None] * Q
+    gam = (d / 16 + 32) * 2.0 ** -24
+    su = np.abs(xv) @ np.abs(w13).T
+    da, dc = gam * su[:, :inter], gam * su[:, inter:]
+    ddh = np.abs(g)[:, None] * gam * (np.abs(dyv) @ np.abs(w2)) + 2.0 ** -22 * np.abs(dh)
+    sg = 1.0 / (1.0 + np.exp(-a))
+    s1 = sg * (1.0 + a * (1.0 - sg))                   # silu'
+    s2 = sg * (1.0 - sg) * (2.0 + a * (1.0 - 2.0 * sg))  # silu''
+    ef = 8 * 2.0 ** -24
+    du_g = dh * c * s1
+    du_u = dh * a * sg
+    e_g = (np.abs(dh * c) * (np.abs(s2) * da + ef * (sg + np.abs(a) * sg * (1 - sg)))
+           + np.abs(dh * s1) * dc + np.abs(c * s1) * ddh + 2.0 ** -8 * np.abs(du_g))
+    e_u = np.abs(dh * s1) * da + np.abs(a * sg) * ddh + 2.0 ** -8 * np.abs(du_u)
+    env = np.concatenate([e_g, e_u], axis=1).T @ np.abs(xv) + 2.0 ** -8 * np.abs(ref)
+    rown = np.abs(ref).max(axis=1, keepdims=True)
+    bar = tol * np.maximum(rown, 1e-6 * rown.max())
+    if got is None:
+        return env, bar
+    return float((np.abs(got - ref) / np.maximum(bar, env)).max())
+
+
 def _sample(T, n):
     return np.array(sorted(set(np.linspace(0, T - 1, n).astype(int))))
 
@@ -138,8 +182,9 @@ def _sample(T, n):
 def test_backward_longcat_shape(name):
     # LongCat shape. (1) A handful of tokens on their own: every output
     # checked (dW13/dW2 on three touched experts, the rest zero). (2) The
-    # full batch: dx on sampled tokens and dW13/dW2 of two experts against
-    # the oracle, and dW_r equal to the sum of the two half batches' dW_r.
+    # full batch: dx on sampled tokens and dW13/dW2 of at least 32 experts
+    # against the oracle, and dW_r equal to the sum of the two half batches'
+    # dW_r.
     cfg, L = layer(name)
     x = inputs.make_tokens(cfg, "cuda")
     dy = inputs.make_upstream_grad(cfg, "cuda")
@@ -159,24 +204,49 @@ def test_backward_longcat_shape(name):
     ref = oracle_backward(cfg, L, x[torch.as_tensor(toks, device="cuda")],
                           dy[torch.as_tensor(toks, device="cuda")], idx[toks])
     err_dx = max_rel_err(res["dx"][torch.as_tensor(toks, device="cuda")].cpu().numpy(), ref["dx"])
-    # weight gradients of the most loaded expert and of the last touched one
+    # weight gradients of at least 32 touched experts spread over the expert
+    # ids and over the row counts (so over the weight-gradient kernel's k
+    # lengths and the dgrad kernel's M tiles): 16 evenly spaced in id order,
+    # 16 evenly spaced in row-count order (the least and most loaded among
+    # them), and the last touched one; every touched expert at decode
     counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)[: cfg.n_ffn]
-    errs = {}
-    for e in sorted({int(np.argmax(counts)), int(np.nonzero(counts)[0][-1])}):
+    touched = np.nonzero(counts)[0]
+    if len(touched) <= 400 and T <= 64:
+        pick = set(int(e) for e in touched)
+    else:
+        by_count = touched[np.argsort(counts[touched], kind="stable")]
+        pick = set(int(e) for e in touched[np.linspace(0, len(touched) - 1, 16).astype(int)])
+        pick |= set(int(e) for e in by_count[np.linspace(0, len(touched) - 1, 16).astype(int)])
+        pick.add(int(touched[-1]))
+    pick = sorted(pick)
+    assert len(pick) >= min(32, len(touched))
+    get = expert_getter(L, "bf16", prefetch=pick)
+    wr = L["w_router"].cpu().numpy()
+    errs, rel13 = {}, {}
+    for e in pick:
         rows, ks = np.nonzero(idx == e)
         xe = x[torch.as_tensor(rows, device="cuda")]
         dye = dy[torch.as_tensor(rows, device="cuda")]
         xv, dyv = bf16_values(xe), bf16_values(dye)
-        z = oracle.router_logits(xv, L["w_router"].cpu().numpy())
+        z = oracle.router_logits(xv, wr)
         g, _ = oracle.softmax_gates(z, idx[rows])
-        w13_e, w2_e = expert_getter(L, "bf16")(e)
-        _, dw13, dw2, _ = oracle.expert_backward(xv, g[np.arange(len(rows)), ks], dyv,
-                                                 w13_e, w2_e)
-        errs[f"dw13[{e}] ({counts[e]} rows)"] = max_rel_err(bf16_values(res["dw13"][e]), dw13)
-        errs[f"dw2[{e}]"] = max_rel_err(bf16_values(res["dw2"][e]), dw2)
-    print(f"{name} T={T}: dx {err_dx:.3e} over {len(toks)} tokens; {errs}")
+        w13_e, w2_e = get(e)
+        ge = g[np.arange(len(rows)), ks]
+        _, dw13, dw2, _ = oracle.expert_backward(xv, ge, dyv, w13_e, w2_e)
+        got13 = bf16_values(res["dw13"][e])
+        rel13[e] = max_rel_err(got13, dw13)
+        # dW13 against tol or its fp32 error envelope (dw13_excess; 1 = at the allowance)
+        errs[(e, int(counts[e]), "dw13")] = TOL * dw13_excess(xv, dyv, ge, w13_e, w2_e, got13, dw13)
+        errs[(e, int(counts[e]), "dw2")] = max_rel_err(bf16_values(res["dw2"][e]), dw2)
+    worst = max(errs, key=errs.get)
+    rc = counts[pick]
+    w13r = max(rel13, key=rel13.get)
+    print(f"{name} T={T}: dx {err_dx:.3e} over {len(toks)} tokens; dW13/dW2 of {len(pick)} of "
+          f"{len(touched)} touched experts (ids {pick[0]}..{pick[-1]}, {rc.min()}..{rc.max()} "
+          f"rows): worst {worst} {errs[worst]:.3e} (dW13 as tol x allowance ratio; plain "
+          f"per-row dW13 worst: expert {w13r} {rel13[w13r]:.3e})")
     assert err_dx < TOL
-    assert max(errs.values()) < TOL, errs
+    assert errs[worst] < TOL, (worst, errs[worst])
     # dW_r is a sum over tokens: full batch = first half + second half. The
     # router's fp32 split-K summation order depends on the batch size, so a
     # token at a near tie may be routed differently in a half batch; such

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from mixture_experts_layer_biased_amd import inputs, lcmoe
-from tests.gpu_common import layer, max_rel_err, oracle_forward_rows
+from tests.gpu_common import (check_fp8a8_chain, cover_tokens, layer, max_rel_err,
+                              oracle_forward_rows)
 from tests.helpers import bf16_values
 
 pytestmark = pytest.mark.gpu
@@ -22,14 +23,27 @@ TOL = {"bf16": 2e-2, "fp8": 5e-2, "fp8a8": 5e-2}
 
 
 def run_forward(cfg, L, x):
+    """lcmoe_forward; with fp8 activations lcmoe_forward_inspect, whose
+    outputs are checked to be those of lcmoe_forward bit for bit and which
+    also returns the activation codes, scales and pre-quantization H."""
     shape = lcmoe.shape_of(cfg)
     res = lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"],
                         L["w13_scale"], L["w2_scale"])
+    if cfg.wdtype == "fp8a8":
+        ins = lcmoe.forward_inspect(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"],
+                                    L["w13_scale"], L["w2_scale"])
+        torch.cuda.synchronize()
+        for k in ("y", "idx", "gate", "counts"):
+            assert torch.equal(ins[k], res[k]), f"lcmoe_forward_inspect {k} differs"
+        res = ins
     torch.cuda.synchronize()
     return res
 
 
 def check_rows(cfg, L, x, res, tokens, cache=None):
+    if cfg.wdtype == "fp8a8":
+        # stage by stage on the GPU's own intermediates (check_fp8a8_chain)
+        return check_fp8a8_chain(cfg, L, x, res, tokens)[1]
     idx = res["idx"].cpu().numpy()
     y_ref = oracle_forward_rows(cfg, L, x, idx, tokens, cache=cache)
     y = bf16_values(res["y"][torch.as_tensor(tokens, device=x.device)])
@@ -60,11 +74,13 @@ def test_forward_all_tokens(name, T):
     check_rows(cfg, L, x, res, np.arange(T), cache={})
 
 
+@pytest.mark.parametrize("inter", [128, 256, 384, 512])
 @pytest.mark.parametrize("T", [1, 33, 300, 4096])
-def test_forward_fp8_activations_all_tokens(T):
-    # fp8 weights and fp8 activations at the small shape: the small-M path
+def test_forward_fp8_activations_all_tokens(T, inter):
+    # fp8 weights and fp8 activations at the small shape, at every intermediate
+    # size from the smallest the boundary accepts (128): the small-M path
     # (dequantized bf16 rows), the mixed regime and the large-M fp8-MFMA path.
-    cfg, L = layer("small", wdtype="fp8a8")
+    cfg, L = layer("small", wdtype="fp8a8", inter=inter)
     x = inputs.make_tokens(cfg, "cuda", tokens=T)
     res = run_forward(cfg, L, x)
     check_routing_consistent(cfg, L, x, res)
@@ -108,18 +124,27 @@ def _sample(x, n, extra_large=0):
     return np.array(sorted(set(toks)))
 
 
-@pytest.mark.parametrize("name,n_sample,n_skew", [("decode", 8, 0), ("prefill", 6, 2),
+@pytest.mark.parametrize("name,n_sample,n_skew", [("decode", 64, 0), ("prefill", 6, 2),
                                                   ("fp8", 5, 0), ("fp8a8", 5, 0),
                                                   ("prefill32k", 4, 0), ("ep8_shard", 6, 0)])
-def test_forward_longcat_shape_sampled(name, n_sample, n_skew):
+def test_forward_longcat_shape_every_expert(name, n_sample, n_skew):
+    # At the LongCat shape, in the launch configuration the bench times: every
+    # decode token; at the larger batches a set of tokens whose selections
+    # touch every FFN expert that the batch touches (so every expert's
+    # weights, M-tiles and column slices feed a checked output), plus evenly
+    # spaced tokens and the x20-scaled ones.
     cfg, L = layer(name)
     x = inputs.make_tokens(cfg, "cuda")
     res = run_forward(cfg, L, x)
     check_routing_consistent(cfg, L, x, res)
     counts = res["counts"].cpu().numpy()
+    toks, touched, covered = cover_tokens(res["idx"].cpu().numpy(), cfg.n_ffn,
+                                          extra=_sample(x, n_sample, n_skew))
     print(f"{name}: mean FFN experts/token {counts[:cfg.n_ffn].sum() / cfg.tokens:.3f}, "
-          f"touched {int((counts[:cfg.n_ffn] > 0).sum())}, max rows {counts[:cfg.n_ffn].max()}")
-    check_rows(cfg, L, x, res, _sample(x, n_sample, n_skew))
+          f"max rows {counts[:cfg.n_ffn].max()}; checking {len(toks)} tokens covering "
+          f"{covered} of {touched} touched FFN experts")
+    assert covered == touched == int((counts[:cfg.n_ffn] > 0).sum())
+    check_rows(cfg, L, x, res, toks)
 
 
 def test_forward_maximum_tokens():
