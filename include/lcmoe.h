@@ -199,6 +199,33 @@ lcmoe_status lcmoe_forward_inspect(const lcmoe_shape* shape, int32_t T, const vo
                                    void* xq, float* xs, void* h, void* hq, float* hs,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the fixed device scratch array lcmoe_forward_noalloc works in. */
+#define LCMOE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* lcmoe_forward for callers that cannot allocate device memory (work under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same outputs, bit for bit, with the workspace
+ * taken from a fixed array of LCMOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each device it runs on (in its code object, from the first use on
+ * that device until the process ends). The call allocates nothing. Arguments
+ * and outputs as lcmoe_forward without ws / ws_bytes; the caller still owns
+ * the inputs and outputs. A call whose workspace for its T (at most
+ * lcmoe_workspace_bytes(shape, T)) exceeds the array returns
+ * LCMOE_ERR_WORKSPACE before anything is enqueued; at the LongCat shape with
+ * bf16 weights that admits up to about 1,000 tokens per call (decode
+ * batches). Every call on one device shares that
+ * device's array: two calls that can overlap on one device (other streams,
+ * other host threads) race and must be ordered by the caller. The stream must
+ * belong to the current device; the first call on a device looks up the
+ * array's address there (LCMOE_ERR_HIP if that fails). */
+lcmoe_status lcmoe_forward_noalloc(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias,
+                                   const void* w13, const float* w13_scale,
+                                   const void* w2, const float* w2_scale,
+                                   void* y_bf16,
+                                   int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                                   hipStream_t stream);
+
 /* Stages of lcmoe_forward, in launch order (for lcmoe_forward_staged). */
 typedef enum {
   LCMOE_STAGE_ROUTER = 0,     /* router logits                          */

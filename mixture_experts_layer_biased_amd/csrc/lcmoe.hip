@@ -4,15 +4,50 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "lcmoe.h"
 #include "kernels.h"
+
+// Workspace of lcmoe_forward_noalloc: one fixed array in the library's code
+// object, so each device that runs the library holds its own copy until the
+// process ends. Host code never passes this name to a kernel (on the host it
+// is a stand-in, not a device address): the device address of each copy
+// comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoallocScratchBytes = LCMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
 using namespace lcmoe;
 
 constexpr size_t kAlign = 256;
+
+// Device addresses of `scratch`, per device id, filled on each device's
+// first no-allocation call with that device current.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+lcmoe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return LCMOE_ERR_HIP;
+  }
+  if (dev >= kMaxDevices) return LCMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return LCMOE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LCMOE_OK;
+}
 
 struct Layout {
   int ks = 1, kchunk = 0, ntile = 0;
@@ -507,6 +542,25 @@ lcmoe_status lcmoe_forward_inspect(const lcmoe_shape* shape, int32_t T, const vo
   o.hs = hs;
   return forward_impl(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale, y_bf16,
                       topk_idx, topk_gate, counts, ws, ws_bytes, stream, nullptr, nullptr, &o);
+}
+
+lcmoe_status lcmoe_forward_noalloc(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
+                                   const float* w_router, const float* bias, const void* w13,
+                                   const float* w13_scale, const void* w2, const float* w2_scale,
+                                   void* y_bf16, int32_t* topk_idx, float* topk_gate,
+                                   int32_t* counts, hipStream_t stream) {
+  lcmoe_status st = check_forward_args(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2,
+                                       w2_scale, y_bf16, topk_idx, topk_gate, counts);
+  if (st != LCMOE_OK) return st;
+  if (T > 0 && make_layout(*shape, T).total > kNoallocScratchBytes) return LCMOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (T > 0) {
+    st = noalloc_scratch(&ws);
+    if (st != LCMOE_OK) return st;
+  }
+  return forward_impl(shape, T, x_bf16, w_router, bias, w13, w13_scale, w2, w2_scale, y_bf16,
+                      topk_idx, topk_gate, counts, ws, ws != nullptr ? kNoallocScratchBytes : 0,
+                      stream, nullptr, nullptr);
 }
 
 size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens) {

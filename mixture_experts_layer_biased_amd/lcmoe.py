@@ -17,7 +17,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 W_BF16, W_FP8_E4M3_B128, W_FP8_E4M3_B128_A8 = 0, 1, 2
 
 EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forward",
-           "lcmoe_forward_staged", "lcmoe_forward_inspect", "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
+           "lcmoe_forward_staged", "lcmoe_forward_inspect", "lcmoe_forward_noalloc",
+           "lcmoe_bias_update", "lcmoe_router_stats_workspace_bytes",
            "lcmoe_router_stats", "lcmoe_backward_workspace_bytes", "lcmoe_backward",
            "lcmoe_backward_staged", "lcmoe_forward_train", "lcmoe_backward_saved",
            "lcmoe_status_str")
@@ -81,6 +82,8 @@ def lib():
     L.lcmoe_forward_staged.restype = st
     L.lcmoe_forward_inspect.argtypes = [S, i32] + [_P] * 17 + [sz, _P]
     L.lcmoe_forward_inspect.restype = st
+    L.lcmoe_forward_noalloc.argtypes = [S, i32] + [_P] * 11 + [_P]
+    L.lcmoe_forward_noalloc.restype = st
     L.lcmoe_bias_update.argtypes = [S, i32, _P, ctypes.c_double, ctypes.c_double, _P, _P]
     L.lcmoe_bias_update.restype = st
     L.lcmoe_router_stats_workspace_bytes.argtypes = [S, i32]
@@ -296,6 +299,34 @@ def forward_inspect(shape, x, w_router, bias, w13, w2, w13_scale, w2_scale, ws=N
                                        _ptr(xs), _ptr(h), _ptr(hq), _ptr(hs), _ptr(ws), ws.numel(),
                                        _stream()), "lcmoe_forward_inspect")
     return dict(y=y, idx=idx, gate=gate, counts=counts, xq=xq, xs=xs, h=h, hq=hq, hs=hs)
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def forward_noalloc(shape, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None, out=None):
+    """lcmoe_forward_noalloc: the forward on the library's fixed per-device
+    scratch array (no workspace argument; the call itself allocates
+    nothing). Output tensors may be passed in `out` (y, idx, gate, counts).
+    Returns dict(y, idx, gate, counts)."""
+    T = x.shape[0]
+    dev = x.device
+    K, E, d = shape.top_k, shape.n_experts, shape.d_model
+    _expect_layer(shape, T, x, w_router, bias)
+    _expect_experts(shape, w13, w2, w13_scale, w2_scale)
+    o = out or {}
+    y = o.get("y", torch.empty(T, d, dtype=torch.bfloat16, device=dev))
+    idx = o.get("idx", torch.empty(T, K, dtype=torch.int32, device=dev))
+    gate = o.get("gate", torch.empty(T, K, dtype=torch.float32, device=dev))
+    counts = o.get("counts", torch.empty(E, dtype=torch.int32, device=dev))
+    _expect("y", y, torch.bfloat16, (T, d))
+    _expect_routing_out(shape, T, idx, gate, counts)
+    _dev(x, w_router, bias, w13, w2, w13_scale, w2_scale, y, idx, gate, counts)
+    _check(lib().lcmoe_forward_noalloc(ctypes.byref(shape), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                       _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                       _ptr(y), _ptr(idx), _ptr(gate), _ptr(counts), _stream()),
+           "lcmoe_forward_noalloc")
+    return dict(y=y, idx=idx, gate=gate, counts=counts)
 
 
 def bias_update(shape, counts, mu, k_e, bias, t_all):

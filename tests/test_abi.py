@@ -161,6 +161,32 @@ def test_workspace_monotone_past_32k_tokens(dims):
         prev_f, prev_b = f, b
 
 
+def test_noalloc_validation():
+    # lcmoe_forward_noalloc validates like lcmoe_forward and rejects a batch
+    # whose workspace exceeds its fixed array, all before any HIP call
+    L = lcmoe.lib()
+
+    def fwd(sh, T, **kw):
+        a = dict(x=FAKE, wr=FAKE, b=FAKE, w13=FAKE, s13=None, w2=FAKE, s2=None, y=FAKE, idx=FAKE,
+                 g=FAKE, c=FAKE)
+        a.update(kw)
+        return L.lcmoe_forward_noalloc(ctypes.byref(sh), T, a["x"], a["wr"], a["b"], a["w13"],
+                                       a["s13"], a["w2"], a["s2"], a["y"], a["idx"], a["g"],
+                                       a["c"], None)
+
+    s = shp()
+    assert fwd(s, -1) == ERR_INVALID_ARG
+    assert fwd(s, 4, c=None) == ERR_INVALID_ARG
+    assert fwd(s, 4, w13=None) == ERR_INVALID_ARG
+    assert fwd(s, 4, y=MIS) == ERR_UNSUPPORTED
+    assert fwd(shp(w_dtype=7), 4) == ERR_INVALID_ARG
+    assert fwd(make_shape(128, 8, 4, 3, 128, 1), 4) == ERR_INVALID_ARG   # fp8 without scales
+    big = make_shape(6144, 512, 256, 12, 2048)
+    assert lcmoe.workspace_bytes(big, 4096) > lcmoe.NOALLOC_SCRATCH_BYTES
+    assert fwd(big, 4096) == ERR_WORKSPACE
+    assert fwd(big, 2 ** 31 // 12 + 1) == ERR_UNSUPPORTED
+
+
 def test_zero_tokens_validation():
     # T = 0 still validates its arguments before anything is enqueued
     s = shp()
