@@ -174,13 +174,18 @@ def pmc_summary(fetch_dir, write_dir, workload, cmd):
                      indent=1))
 
 
-def trace_summary(trace_dir, workload, cmd, out_path):
+def trace_summary(trace_dir, workload, cmd, out_path, work_path=None):
     """Write the rocprofv3 --kernel-trace --stats summary of the layer's
-    kernels (calls, average / min / max duration) as a markdown table."""
+    kernels (calls, average / min / max duration) as a markdown table. With
+    the work file the profiled bench run wrote (--work-out), also each
+    grouped-GEMM stage's roofline fraction from the rocprof durations of the
+    timed launches (the last `steps` dispatches of its kernel), next to the
+    bench's own event timing of the same launches."""
     import csv
     mapper = bwd_stage_of_kernel if workload.startswith("backward") else stage_of_kernel
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
     lines = [f"# rocprofv3 kernel statistics: {workload} workload", "",
+             f"GEMM source hash (common.h, kernels.h, gemm.hip): `{source_hash()}`", "",
              "Command (from the repository root on the GPU host):", "", "```", cmd, "```", "",
              "| kernel | stage | calls | average us | min us | max us | share % |",
              "|---|---|---|---|---|---|---|"]
@@ -193,6 +198,105 @@ def trace_summary(trace_dir, workload, cmd, out_path):
         lines.append(f"| `{short}` | {st or 'device copies (setup, calibration, backward x copies)'} | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    if work_path and os.path.exists(work_path):
+        work = json.load(open(work_path))
+        steps = int(work["steps"])
+        trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+        durs = {}
+        for r in trace:
+            st = mapper(r["Kernel_Name"])
+            if st is not None:
+                durs.setdefault(st, []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", f"Roofline of the grouped-GEMM stages over the {steps} timed launches "
+                  "(algorithmic bytes: touched experts' weights once, plus the token rows once for "
+                  "gate/up; spills are the gathered per-slot rows, H and Y; peaks 8 TB/s HBM, "
+                  f"{mfma_peak_name(work['wdtype'])} MFMA):", "",
+                  "| stage | rocprof mean ms | bench event mean ms | algorithmic GB | spill GB | "
+                  "TFLOP | bound | achieved | frac (rocprof) | frac (bench) |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
+        for st, w in work["stage_work"].items():
+            if st not in durs or w["flops"] == 0:
+                continue
+            d = [x[1] for x in sorted(durs[st])][-steps:]
+            ms = float(np.mean(d)) / 1e6
+            peak_m = PEAK_FP8 if work["wdtype"] == "fp8a8" else PEAK_BF16
+            bound = "hbm" if w["flops"] / max(w["bytes"], 1) < peak_m / PEAK_HBM else "mfma"
+            if bound == "hbm":
+                ach, peak, unit = w["bytes"] / (ms / 1e3) / 1e9, PEAK_HBM / 1e9, "GB/s"
+                fb = w["bytes"] / (w["ms"] / 1e3) / 1e9 / peak
+            else:
+                ach, peak, unit = w["flops"] / (ms / 1e3) / 1e12, peak_m / 1e12, "TFLOP/s"
+                fb = w["flops"] / (w["ms"] / 1e3) / 1e12 / peak
+            lines.append(f"| {st} | {ms:.3f} | {w['ms']:.3f} | {w['bytes'] / 1e9:.2f} | "
+                         f"{w['spill_bytes'] / 1e9:.2f} | {w['flops'] / 1e12:.2f} | {bound} | "
+                         f"{ach:.0f} {unit} | {ach / peak:.3f} | {fb:.3f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def mfma_peak_name(wdtype):
+    return "5.0 PFLOP/s fp8" if wdtype == "fp8a8" else "2.5 PFLOP/s bf16"
+
+
+def counter_summary(dirs, workload, cmd, out_path, regex="gemm_big"):
+    """Fold rocprofv3 --pmc runs (one counter set per directory) into a
+    markdown table per kernel (mean per launch) with derived figures: the
+    average clock over the launch, the MFMA pipes' busy share of all SIMD
+    cycles, the share of wave cycles spent waiting and issuing VALU work, and
+    the texture-data unit's busy and L2-stall shares. Stamped with the GEMM
+    source hash."""
+    import collections
+    import csv
+    vals = collections.defaultdict(list)
+    kern_ms = {}
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            vals[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+            kern_ms.setdefault(k, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    kernels = sorted({k for k, _ in vals})
+    counters = sorted({c for _, c in vals})
+    m = {(k, c): float(np.mean(v)) for (k, c), v in vals.items()}
+    lines = [f"# rocprofv3 counters: {workload} workload", "",
+             f"GEMM source hash (common.h, kernels.h, gemm.hip): `{source_hash()}`", "",
+             "Commands (from the repository root on the GPU host; one counter set per run):", "",
+             "```"] + cmd.split(" ;; ") + ["```", "", "Mean per launch:", "",
+             "| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+             "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(f"{m.get((k, c), float('nan')):.4g}" for k in kernels)
+                     + " |")
+    lines += ["", "Derived (GRBM_GUI_ACTIVE is the sum over the 8 XCDs, SQ_VALU_MFMA_BUSY_CYCLES over "
+              "the 1024 SIMDs, TA/TD sums over the 256 CUs; wave-cycle shares are of SQ_WAVE_CYCLES):", ""]
+    for k in kernels:
+        g = m.get((k, "GRBM_GUI_ACTIVE"))
+        if not g:
+            continue
+        cyc = g / 8
+        ms = float(np.median(kern_ms[k]))
+        parts = [f"clock {cyc / (ms / 1e3) / 1e9:.2f} GHz over {ms:.2f} ms"]
+        if (k, "SQ_VALU_MFMA_BUSY_CYCLES") in m:
+            parts.append(f"MFMA pipes busy {100 * m[(k, 'SQ_VALU_MFMA_BUSY_CYCLES')] / 1024 / cyc:.1f}% "
+                         "of SIMD cycles")
+        wc = m.get((k, "SQ_WAVE_CYCLES"))
+        if wc:
+            for c, what in (("SQ_WAIT_ANY", "waiting"), ("SQ_ACTIVE_INST_VALU", "issuing VALU"),
+                            ("SQ_ACTIVE_INST_LDS", "issuing LDS")):
+                if (k, c) in m:
+                    parts.append(f"{what} {100 * m[(k, c)] / wc:.1f}% of wave cycles")
+        if (k, "SQ_INSTS_MFMA") in m and (k, "SQ_INSTS_VALU") in m:
+            mf = m[(k, "SQ_INSTS_MFMA")]
+            parts.append(f"{(m[(k, 'SQ_INSTS_VALU')] - mf) / mf:.2f} other VALU instructions per MFMA")
+            if (k, "SQ_INSTS_VALU_CVT") in m:
+                parts.append(f"{m[(k, 'SQ_INSTS_VALU_CVT')] / mf:.2f} conversions per MFMA")
+        for c, what in (("TA_TA_BUSY_sum", "TA busy"), ("TD_TD_BUSY_sum", "TD busy"),
+                        ("TD_TC_STALL_sum", "TD stalled on L2 data")):
+            if (k, c) in m:
+                parts.append(f"{what} {100 * m[(k, c)] / 256 / cyc:.1f}% of CU cycles")
+        lines.append(f"- `{k}`: " + "; ".join(parts) + ".")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -230,13 +334,15 @@ def stage_ms(hip, sets, n_stages):
     return out.mean(axis=0)
 
 
-def kernel_work(cfg, counts):
+def kernel_work(cfg, counts, idx=None):
     """Algorithmic bytes and MFMA flops of each grouped-GEMM stage.
 
-    Per expert touched on a path, its weights once (bf16 2 B, fp8 1 B plus
-    scales); per routed row, the input row read once and the output row
-    written once. Gate/up: 2I*d weights, reads d, writes I per row; down:
-    d*I weights, reads I, writes d per row. Flops 2*rows*(weights).
+    What the method must move: each touched expert's weights read once (bf16
+    2 B, fp8 1 B plus the 128x128 block scales), and for gate/up the token
+    rows that feed it read once (the distinct tokens with a slot on that
+    path; every token when idx is not given). The gathered per-slot copies of
+    those rows, H and Y are the implementation's intermediates: reported as
+    spill_bytes, not counted. Flops 2 * rows * (weights per expert).
     """
     N, d, I = cfg.n_ffn, cfg.d, cfg.inter
     c = counts[:N].astype(np.int64)
@@ -245,11 +351,18 @@ def kernel_work(cfg, counts):
     out = {}
     for path, sel in (("small", (c >= 1) & (c <= 32)), ("large", c > 32)):
         et, rows = int(sel.sum()), int(c[sel].sum())
+        if idx is None:
+            toks = cfg.tokens if rows else 0
+        else:
+            on_path = np.isin(idx, np.nonzero(sel)[0])
+            toks = int(on_path.any(axis=1).sum())
         out[f"gateup_{path}"] = dict(
-            bytes=et * 2 * I * d * (sw + sc) + rows * d * 2 + rows * I * 2,
+            bytes=et * 2 * I * d * (sw + sc) + toks * d * 2,
+            spill_bytes=max(rows - toks, 0) * d * 2 + rows * I * 2,
             flops=2.0 * rows * 2 * I * d, experts=et, rows=rows)
         out[f"down_{path}"] = dict(
-            bytes=et * d * I * (sw + sc) + rows * I * 2 + rows * d * 2,
+            bytes=et * d * I * (sw + sc),
+            spill_bytes=rows * I * 2 + rows * d * 2,
             flops=2.0 * rows * I * d, experts=et, rows=rows)
     return out
 
@@ -303,7 +416,7 @@ def measure(cfg, steps, warmup, hip):
             hip.hipEventDestroy(arr[i])
     counts = out["counts"].cpu().numpy()
     ms = total_ms / steps
-    work = kernel_work(cfg, counts)
+    work = kernel_work(cfg, counts, out["idx"].cpu().numpy())
     stages = {name: float(per_stage[i]) for i, name in enumerate(lcmoe.STAGES)}
     gemm = [k for k in work if work[k]["rows"] > 0]
     dom = max(gemm, key=lambda k: stages[k])
@@ -329,7 +442,9 @@ def measure(cfg, steps, warmup, hip):
         dominant_kernel=dom,
         roofline=dict(bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                       traffic=measured_traffic(cfg.name, dom), algorithmic_bytes=wk["bytes"],
-                      flops=wk["flops"], kernel_ms=stages[dom]),
+                      spill_bytes=wk["spill_bytes"], flops=wk["flops"], kernel_ms=stages[dom]),
+        stage_work={k: dict(bytes=v["bytes"], spill_bytes=v["spill_bytes"], flops=v["flops"],
+                            ms=stages[k]) for k, v in work.items()},
         grouped_gemm=dict(ms=gemm_s * 1e3, mfma_frac=gemm_flops / gemm_s / peak_mfma,
                           hbm_frac=gemm_bytes / gemm_s / PEAK_HBM),
         layer=dict(algorithmic_bytes=lb, hbm_frac=lb / (ms / 1e3) / PEAK_HBM,
@@ -634,11 +749,13 @@ def cpu_baseline(cfg, L, x, out, n_experts_sample):
         _ = r["g"][rows, ks][:, None] * oracle.expert_ffn(xv[rows], w13, w2)
     t_exp = time.perf_counter() - t1
     est = t_route + t_exp * len(touched) / max(1, len(sample))
-    return dict(value=T / est, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=(f"{cfg.name} workload (T={T}): router, selection and gates for all "
+    return dict(value=T / est, unit="tokens/s", cores=int(threads), kind="oracle", projected=True,
+                sample=(f"projected from a sample of the {cfg.name} workload (T={T}): router, "
+                        f"selection and gates for all "
                         f"tokens ({t_route:.1f} s) + SiLU-gated FFN of {len(sample)} of "
                         f"{len(touched)} touched experts on all their routed tokens "
-                        f"({t_exp:.1f} s), expert time scaled by {len(touched)}/{len(sample)}"),
+                        f"({t_exp:.1f} s), expert time scaled by {len(touched)}/{len(sample)}; "
+                        f"the combine (per token a sum of K rows) not timed"),
                 measured_s=t_route + t_exp)
 
 
@@ -663,15 +780,25 @@ def main():
                     help="fold rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="write a rocprofv3 --stats summary to profiles/")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR",
+                    help="fold rocprofv3 --pmc runs into profiles/counters_<workload>.md")
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--work-out", default=None,
+                    help="write the measured workload's per-stage algorithmic work and event "
+                         "timings to this JSON file (read by --trace-summary --work)")
+    ap.add_argument("--work", default=None, help="work file for --trace-summary")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.cmd)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.workload, args.cmd,
-                      os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.md"))
+                      os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.md"), args.work)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.workload, args.cmd,
+                        os.path.join(ROOT, "profiles", f"counters_{args.workload}.md"))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -699,6 +826,10 @@ def main():
         cfg = inputs.CONFIGS[name]
         res, keep = measure(cfg, args.steps, args.warmup, hip)
         results[name] = res
+        if args.work_out and name == names[0]:
+            with open(args.work_out, "w") as f:
+                json.dump(dict(workload=name, wdtype=cfg.wdtype, steps=args.steps,
+                               warmup=args.warmup, stage_work=res["stage_work"]), f, indent=1)
         if args.vendor_gemm:
             res["vendor_gemm"] = vendor_gemm(cfg, keep[2]["counts"].cpu().numpy(), res["stages_ms"])
             if res["vendor_gemm"]:
