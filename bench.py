@@ -592,6 +592,10 @@ def measure_backward(cfg, L, x, steps, warmup, hip):
         lcmoe.backward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"], dy, ws=ws, out=out,
                        stage_events=ev)
 
+    # lcmoe_backward (the weight-gradient GEMMs on a second stream beside the
+    # data-gradient GEMM) for the step time; then the staged entry point, which
+    # runs the same kernels one after another on one stream with events
+    # between them, for the per-stage times
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -599,10 +603,16 @@ def measure_backward(cfg, L, x, steps, warmup, hip):
     b = torch.cuda.Event(enable_timing=True)
     a.record()
     for s in range(steps):
-        step(sets[s])
+        step()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
+    a.record()
+    for s in range(steps):
+        step(sets[s])
+    b.record()
+    torch.cuda.synchronize()
+    seq_ms = a.elapsed_time(b) / steps
     per_stage = stage_ms(hip, sets, nst)
     for arr in sets:
         for i in range(nst + 1):
@@ -647,7 +657,8 @@ def measure_backward(cfg, L, x, steps, warmup, hip):
                                                 L["w2"], dy, ws=ws, out=out, u_saved=u), steps)
     del ws, out, dy, u, fws
     torch.cuda.empty_cache()
-    return dict(tokens=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), stages_ms=stages,
+    return dict(tokens=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), sequential_ms=seq_ms,
+                stages_ms=stages,
                 training_pair=dict(forward_train_ms=fwd_train_ms, backward_saved_ms=bwd_saved_ms,
                                    step_ms=fwd_train_ms + bwd_saved_ms),
                 stage_roofline=roof, dominant_kernel=dom,
@@ -848,7 +859,7 @@ def main():
             res["backward"] = measure_backward(cfg, keep[0], keep[1], args.steps, args.warmup,
                                                hip)
             bw = res["backward"]
-            print(f"[bench] {name} backward: {bw['ms_per_step']:.3f} ms/step, dominant "
+            print(f"[bench] {name} backward: {bw['ms_per_step']:.3f} ms/step (stages in sequence {bw['sequential_ms']:.3f}), dominant "
                   f"{bw['dominant_kernel']} {bw['roofline']['frac']:.3f} of "
                   f"{bw['roofline']['bound']}; training pair: forward with saved u "
                   f"{bw['training_pair']['forward_train_ms']:.3f} ms + backward from it "
@@ -889,8 +900,8 @@ def main():
         "dominant_kernel": m["dominant_kernel"],
         "cpu_baseline": baseline,
         "backward": ({k: results["prefill"]["backward"][k] for k in
-                      ("tokens", "ms_per_step", "tokens_per_s", "dominant_kernel", "roofline",
-                       "training_pair")}
+                      ("tokens", "ms_per_step", "sequential_ms", "tokens_per_s",
+                       "dominant_kernel", "roofline", "training_pair")}
                      if "backward" in results.get("prefill", {}) else None),
         "copy_gbps": copy_gbps,
         "detail": results,

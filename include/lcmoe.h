@@ -21,12 +21,16 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to row-major contiguous arrays
- *     owned by the caller. The library keeps no device memory between calls;
- *     scratch space is the caller's workspace `ws` of `ws_bytes` bytes (at
- *     least lcmoe_workspace_bytes(shape, T)).
+ *     owned by the caller. The library keeps no device memory between calls
+ *     (lcmoe_forward_noalloc's fixed array aside); scratch space is the
+ *     caller's workspace `ws` of `ws_bytes` bytes (at least
+ *     lcmoe_workspace_bytes(shape, T)).
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     Outputs are fully overwritten. Two calls that share a workspace must
- *     be ordered (same stream); there is no global mutable state.
+ *     be ordered (same stream). lcmoe_backward also runs part of its work on
+ *     a second stream of default priority that the library creates once per
+ *     device, forked from and joined back to `stream` with events inside the
+ *     call; everything it enqueues is ordered before later work on `stream`.
  *   - Expert ids 0..N-1 are FFN experts, N..N+Z-1 zero-computation experts.
  *   - bf16 tensors are passed as raw 16-bit storage (`const void*`).
  *   - fp8 weights (LCMOE_W_FP8_E4M3_B128) are OCP E4M3FN codes (one byte
@@ -293,7 +297,12 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
  *   ws         >= lcmoe_backward_workspace_bytes(shape, T) bytes
  * Errors as lcmoe_forward; UNSUPPORTED for fp8 weights and for
  * T * max(d, 2I) * 2 >= 2^32 (the grouped GEMMs address an expert's slot
- * rows with 32-bit byte offsets). T = 0 zeroes the weight gradients. */
+ * rows with 32-bit byte offsets). T = 0 zeroes the weight gradients.
+ * The weight-gradient GEMMs (dW2, dW13; HBM writes) run on the library's
+ * second stream, on part of the CUs, beside dx and the router gradients
+ * (HBM reads) on `stream`; the call joins them back before returning, so
+ * the outputs are ordered on `stream` like any other work. The staged
+ * variant runs every stage in order on `stream` (same kernels, same bits). */
 size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens);
 lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                             const float* w_router, const float* bias, const void* w13,

@@ -293,16 +293,12 @@ void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate
   const int grid = std::max(1, std::min(2048, (T + 3) / 4));
   bwd_router_dz_kernel<<<grid, 256, 0, s>>>(logits, idx, gate, dg, T, E, Ep, K, dzp, dzt);
 }
-bool launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_t* x,
-                         const float* wr, int T, int E, int Ep, int d, uint16_t* wsp,
-                         uint16_t* x3, int* rg, float* dwr, float* dxr, hipStream_t s) {
+void launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_t* x,
+                         const float* wr, int T, int E, int Ep, int d, uint16_t* wsp, int* rg,
+                         float* dwr, float* dxr, hipStream_t s) {
   const long long n4 = (long long)Ep * d / 4;
   router_w_split_kernel<<<(int)std::min<long long>(4096, (n4 + 255) / 256), 256, 0, s>>>(
       wr, E, Ep, d, T, wsp, rg);
-  for (int j = 0; j < 3; ++j)
-    if (hipMemcpyAsync(x3 + (size_t)j * T * d, x, (size_t)T * d * 2, hipMemcpyDeviceToDevice, s) !=
-        hipSuccess)
-      return false;
   BwdGemmArgs g{};
   g.n_ffn = 1;
   // dx_r[t][c] = sum over the six plane products of dz[t][i] W_r[i][c]
@@ -311,15 +307,14 @@ bool launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_
   g.c = dxr; g.c_ld = d; g.N = d; g.K = 6 * Ep;
   g.counts = rg; g.offsets = rg + 1; g.tile_prefix = rg + 2;
   launch_bwd_dgrad(g, kBwdRouterDx, bwd_dgrad_grid(T, 1, d), s);
-  // dW_r[i][c] = sum over the 3 T plane rows of dz[t][i] x[t][c]
+  // dW_r[i][c] = sum over the 3 T plane rows k of dz[k][i] x[k mod T][c]
   BwdGemmArgs w{};
   w.n_ffn = 1;
   w.a = dzt; w.a_ld = Ep;
-  w.b = x3; w.b_ld = d;
+  w.b = x; w.b_ld = d; w.b_wrap = T;
   w.c = dwr; w.c_ld = d; w.M = Ep; w.m_store = E; w.N = d;
   w.counts = rg + 4; w.offsets = rg + 5;
   launch_bwd_wgrad_f32(w, s);
-  return true;
 }
 void launch_bwd_dx(const float* dXs, const uint16_t* dy, const float* dxr, const int* row_of_slot,
                    const float* gate, int T, int d, int K, float* dx, hipStream_t s) {

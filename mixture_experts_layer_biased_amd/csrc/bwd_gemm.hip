@@ -260,6 +260,9 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_f32_kernel(BwdGemmArgs
     voff[j] = (uint32_t)(col * 2);
   }
 
+  // With b_wrap > 0, B row k is row k mod b_wrap (the router's dW_r: the
+  // three dz planes stacked along k all multiply x, read in place).
+  const int bwrap = g.b_wrap;
   auto issue = [&](int s) {
     const int k0 = s * BK;
     const int kmax = K - 1 - k0;  // rows past K re-load row K - 1
@@ -269,8 +272,13 @@ __global__ __launch_bounds__(64 * WM * WN) void bwd_wgrad_f32_kernel(BwdGemmArgs
       const bool isA = j < JA;
       const long long ld = isA ? g.a_ld : g.b_ld;
       const int k = krow[j] < kmax ? krow[j] : kmax;
-      bdma16((isA ? abase : bbase) + (size_t)k0 * ld * 2, voff[j] + (uint32_t)(k * ld * 2),
-             slot + 64 * (wave + NW * j));
+      if (!isA && bwrap > 0) {
+        const int kr = (k0 + k) % bwrap;
+        bdma16(bbase, voff[j] + (uint32_t)kr * (uint32_t)(ld * 2), slot + 64 * (wave + NW * j));
+      } else {
+        bdma16((isA ? abase : bbase) + (size_t)k0 * ld * 2, voff[j] + (uint32_t)(k * ld * 2),
+               slot + 64 * (wave + NW * j));
+      }
     }
   };
 
@@ -783,10 +791,7 @@ int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols) {
   const long long items = (smax / kBwdTileM + n_ffn) * ((n_cols + kBwdTileNDgrad - 1) / kBwdTileNDgrad);
   return (int)std::min<long long>(items + 8, 1ll << 30);
 }
-// Grid of the persistent weight-gradient launch: one block per CU (its LDS
-// ring takes most of a CU's 160 KB), a multiple of 8 for the per-XCD
-// layout, and no more blocks than tiles allow.
-int bwd_wgrad_grid(int n_ffn, int M, int N) {
+int bwd_device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -795,9 +800,17 @@ int bwd_wgrad_grid(int n_ffn, int M, int N) {
       n = 256;
     cus = n;
   }
+  return cus;
+}
+// Grid of the persistent weight-gradient launch: one block per CU (its LDS
+// ring takes most of a CU's 160 KB), or max_blocks when given, a multiple of
+// 8 for the per-XCD layout, and no more blocks than tiles allow.
+int bwd_wgrad_grid(int n_ffn, int M, int N, int max_blocks) {
+  const int cus = bwd_device_cus();
   const long long items = (long long)n_ffn * ((M + kWgradBM - 1) / kWgradBM) *
                           ((N + kWgradBN - 1) / kWgradBN);
-  const long long blocks = std::min<long long>((cus + 7) / 8 * 8, (items + 7) / 8 * 8);
+  long long blocks = std::min<long long>((cus + 7) / 8 * 8, (items + 7) / 8 * 8);
+  if (max_blocks > 0) blocks = std::min<long long>(blocks, max_blocks / 8 * 8);
   return (int)std::max<long long>(8, blocks);
 }
 

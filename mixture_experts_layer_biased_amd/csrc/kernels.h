@@ -101,9 +101,14 @@ struct BwdGemmArgs {
   const int* offsets;
   const int* tile_prefix;  // [N+1] prefix of ceil(count / kBwdTileM) (dgrad)
   int n_ffn;
+  int b_wrap;              // f32 wgrad: B row k is row k mod b_wrap (0: no wrap)
 };
 int bwd_dgrad_grid(long long smax, int n_ffn, int n_cols);
-int bwd_wgrad_grid(int n_ffn, int M, int N);
+// Persistent weight-gradient grid: one block per CU, at most max_blocks when
+// max_blocks > 0 (a multiple of 8).
+int bwd_wgrad_grid(int n_ffn, int M, int N, int max_blocks = 0);
+// Compute units of the current device (256 if the query fails).
+int bwd_device_cus();
 // The backward's grouped GEMMs on the ring kernel (dgrad, weights read
 // k-major: W2^T dy, dU W13, the router's dz W_r; wgrad: the weight
 // gradients, dW_r).
@@ -130,11 +135,12 @@ void launch_bwd_zero_dg(const uint16_t* x, const uint16_t* dy, const int* idx, i
                         int N, float* dg, hipStream_t s);
 void launch_bwd_router_dz(const float* logits, const int* idx, const float* gate, const float* dg,
                           int T, int E, int Ep, int K, uint16_t* dzp, uint16_t* dzt, hipStream_t s);
-// Router gradients on bf16 MFMA from exact planes: dx_r = dz W_r, dW_r = dz^T x.
-// wsp [6 Ep][d], x3 [3 T][d] and rg [6] are scratch. Returns false if a copy fails.
-bool launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_t* x,
-                         const float* wr, int T, int E, int Ep, int d, uint16_t* wsp,
-                         uint16_t* x3, int* rg, float* dwr, float* dxr, hipStream_t s);
+// Router gradients on bf16 MFMA from exact planes: dx_r = dz W_r, dW_r = dz^T x
+// (the three dz planes stacked along k, x read in place for each).
+// wsp [6 Ep][d] and rg [6] are scratch.
+void launch_router_grads(const uint16_t* dzp, const uint16_t* dzt, const uint16_t* x,
+                         const float* wr, int T, int E, int Ep, int d, uint16_t* wsp, int* rg,
+                         float* dwr, float* dxr, hipStream_t s);
 void launch_bwd_dx(const float* dXs, const uint16_t* dy, const float* dxr, const int* row_of_slot,
                    const float* gate, int T, int d, int K, float* dx, hipStream_t s);
 

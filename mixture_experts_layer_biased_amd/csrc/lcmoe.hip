@@ -135,7 +135,7 @@ Layout make_layout(const lcmoe_shape& s, int T) {
 struct BwdLayout {
   Layout f;
   size_t idx = 0, gate = 0, counts = 0, logits = 0, tprefix = 0, bprefix = 0, bmeta = 0, Xs = 0,
-         dYs = 0, Q = 0, dU = 0, Hg = 0, dgp = 0, dXs = 0, dg = 0, dzp = 0, dzt = 0, wsp = 0, x3 = 0,
+         dYs = 0, Q = 0, dU = 0, Hg = 0, dgp = 0, dXs = 0, dg = 0, dzp = 0, dzt = 0, wsp = 0,
          rg = 0, dxr = 0, total = 0;
   int nslices = 0;  // 128-column blocks of the gate/up pass (dg partials per row: 4 per block)
   int Ep = 0;  // experts padded to a multiple of 64 (router-gradient planes)
@@ -172,12 +172,55 @@ BwdLayout make_bwd_layout(const lcmoe_shape& s, int T) {
   B.dzp = take((size_t)T * 6 * B.Ep * 2);
   B.dzt = take((size_t)3 * T * B.Ep * 2);
   B.wsp = take((size_t)6 * B.Ep * d * 2);
-  B.x3 = take((size_t)3 * T * d * 2);
   B.rg = take(64);
   B.dxr = take((size_t)T * d * 4);
   B.total = off;
   return B;
 }
+
+// The backward's second stream, per device id: the weight-gradient GEMMs
+// (write-bound) run on it beside the data-gradient GEMM (read-bound) on the
+// caller's stream, forked and joined with events. Default priority. Created
+// on a device's first backward call with that device current; g_aux_mu is
+// held from the fork to the join of each call, so calls from several host
+// threads never interleave their use of the events.
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_aux_mu;
+AuxStream g_aux[kMaxDevices];
+
+lcmoe_status aux_stream(AuxStream** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return LCMOE_ERR_HIP;
+  }
+  if (dev >= kMaxDevices) return LCMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  AuxStream& a = g_aux[dev];
+  if (a.s == nullptr) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      return LCMOE_ERR_HIP;
+    }
+    a.s = s;
+    a.fork = f;
+    a.join = j;
+  }
+  *out = &a;
+  return LCMOE_OK;
+}
+
+// Share of the CUs (in eighths) the weight-gradient GEMMs run on while the
+// data-gradient GEMM runs beside them (measured at the LongCat prefill batch:
+// 4/8 and 8/8 slower, 5/8 and 6/8 within 1%).
+constexpr int kBwdWgradEighths = 6;
 
 // Largest layout over every T <= tmax, so a workspace sized for tmax serves
 // any smaller call and the size is non-decreasing in tmax. Every region
@@ -611,6 +654,11 @@ lcmoe_status backward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf
   const Layout& L = B.f;
   char* base = ws_base(ws, ws_bytes, B.total);
   if (base == nullptr) return LCMOE_ERR_WORKSPACE;
+  AuxStream* aux = nullptr;  // stage events time the stages in order, on one stream
+  if (ev == nullptr) {
+    lcmoe_status sa = aux_stream(&aux);
+    if (sa != LCMOE_OK) return sa;
+  }
   clear_hip_error();
 
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
@@ -707,37 +755,66 @@ lcmoe_status backward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf
   launch_bwd_router_dz(logits, idx, gate, dg, T, E, B.Ep, K, dzp, dzt, stream);
   mark(ev, 4, stream);
 
-  // 5. dX per slot row = dU_e W13_e (W13 read k-major)
-  g.a = dU; g.a_ld = 2 * I;
-  g.b = static_cast<const uint16_t*>(w13); g.b_ld = d; g.b_estride = (long long)2 * I * d;
-  g.c = dXs; g.c_ld = d; g.N = d; g.K = 2 * I;
-  launch_bwd_dgrad(g, kBwdDx, bwd_dgrad_grid(smax, N, d), stream);
-  mark(ev, 5, stream);
-
-  // 6. dW2_e[c][j] = sum over the expert's slots of dy[t][c] (g h)[s][j]
-  g.a = dYs; g.a_ld = d;
-  g.b = Hg; g.b_ld = I; g.b_estride = 0;
-  g.c = dw2; g.c_ld = I; g.M = d; g.m_store = d; g.N = I;
-  launch_bwd_wgrad(g, kBwdDw2, bwd_wgrad_grid(N, d, I), stream);
-  mark(ev, 6, stream);
-
-  // 7. dW13_e[r][c] = sum over the expert's slots of dU[s][r] x[t][c]
-  g.a = dU; g.a_ld = 2 * I;
-  g.b = Xs; g.b_ld = d;
-  g.c = dw13; g.c_ld = d; g.M = 2 * I; g.m_store = 2 * I; g.N = d;
-  launch_bwd_wgrad(g, kBwdDw13, bwd_wgrad_grid(N, 2 * I, d), stream);
-  mark(ev, 7, stream);
-
-  // 8. router: dW_r = dz^T x, dx_r = dz W_r on bf16 MFMA from exact planes of dz
-  //    and W_r (fp32 accumulation)
-  if (!launch_router_grads(dzp, dzt, x, w_router, T, E, B.Ep, d, at<uint16_t>(base, B.wsp),
-                           at<uint16_t>(base, B.x3), at<int>(base, B.rg), dw_router, dxr, stream))
+  // 5.-9. dX per slot row = dU_e W13_e (W13 read k-major); dW2_e[c][j] = sum
+  // over the expert's slots of dy[t][c] (g h)[s][j]; dW13_e[r][c] = sum over
+  // the expert's slots of dU[s][r] x[t][c]; the router gradients dW_r = dz^T x
+  // and dx_r = dz W_r (bf16 MFMA on exact planes of dz and W_r, fp32
+  // accumulation); dx. The weight gradients depend on nothing after step 4
+  // and nothing after them depends on them, so without stage events they go
+  // to the second stream on part of the CUs (HBM writes) while dX and the
+  // router gradients run on the caller's stream (HBM reads).
+  auto dx_rows = [&](hipStream_t s) {
+    BwdGemmArgs h = g;
+    h.a = dU; h.a_ld = 2 * I;
+    h.b = static_cast<const uint16_t*>(w13); h.b_ld = d; h.b_estride = (long long)2 * I * d;
+    h.c = dXs; h.c_ld = d; h.N = d; h.K = 2 * I;
+    launch_bwd_dgrad(h, kBwdDx, bwd_dgrad_grid(smax, N, d), s);
+  };
+  auto wgrad = [&](BwdOp op, hipStream_t s, int max_blocks) {
+    BwdGemmArgs h = g;
+    if (op == kBwdDw2) {
+      h.a = dYs; h.a_ld = d;
+      h.b = Hg; h.b_ld = I; h.b_estride = 0;
+      h.c = dw2; h.c_ld = I; h.M = d; h.m_store = d; h.N = I;
+    } else {
+      h.a = dU; h.a_ld = 2 * I;
+      h.b = Xs; h.b_ld = d; h.b_estride = 0;
+      h.c = dw13; h.c_ld = d; h.M = 2 * I; h.m_store = 2 * I; h.N = d;
+    }
+    launch_bwd_wgrad(h, op, bwd_wgrad_grid(N, h.M, h.N, max_blocks), s);
+  };
+  auto router = [&](hipStream_t s) {
+    launch_router_grads(dzp, dzt, x, w_router, T, E, B.Ep, d, at<uint16_t>(base, B.wsp),
+                        at<int>(base, B.rg), dw_router, dxr, s);
+  };
+  auto dx_final = [&](hipStream_t s) {
+    launch_bwd_dx(dXs, dy, dxr, row_of_slot, gate, T, d, K, dx, s);
+  };
+  if (aux == nullptr) {
+    dx_rows(stream);
+    mark(ev, 5, stream);
+    wgrad(kBwdDw2, stream, 0);
+    mark(ev, 6, stream);
+    wgrad(kBwdDw13, stream, 0);
+    mark(ev, 7, stream);
+    router(stream);
+    mark(ev, 8, stream);
+    dx_final(stream);
+    mark(ev, 9, stream);
+    return hip_status();
+  }
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  if (hipEventRecord(aux->fork, stream) != hipSuccess ||
+      hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
     return LCMOE_ERR_HIP;
-  mark(ev, 8, stream);
-
-  // 9. dx
-  launch_bwd_dx(dXs, dy, dxr, row_of_slot, gate, T, d, K, dx, stream);
-  mark(ev, 9, stream);
+  const int share = std::max(8, bwd_device_cus() * kBwdWgradEighths / 8 / 8 * 8);
+  wgrad(kBwdDw2, aux->s, share);
+  wgrad(kBwdDw13, aux->s, share);
+  if (hipEventRecord(aux->join, aux->s) != hipSuccess) return LCMOE_ERR_HIP;
+  dx_rows(stream);
+  router(stream);
+  dx_final(stream);
+  if (hipStreamWaitEvent(stream, aux->join, 0) != hipSuccess) return LCMOE_ERR_HIP;
   return hip_status();
 }
 
