@@ -11,7 +11,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblcmoe.so")
+# The in-tree build; LCMOE_LIBRARY names another build of the same library
+# (the host-sanitizer build of build_sanitized.py).
+LIB_PATH = os.environ.get("LCMOE_LIBRARY") or os.path.join(_PKG, "liblcmoe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 W_BF16, W_FP8_E4M3_B128, W_FP8_E4M3_B128_A8 = 0, 1, 2
