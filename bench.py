@@ -783,7 +783,7 @@ def main():
                     help="skip the backward measurement on the bf16 prefill batch")
     ap.add_argument("--backward-only", action="store_true",
                     help="measure only the backward on the prefill batch (for profiling runs)")
-    ap.add_argument("--cpu-experts", type=int, default=160)
+    ap.add_argument("--cpu-experts", type=int, default=240)
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time the vendor library's dense batched product at the large-path "
                          "shape of each bf16 workload (context, not part of the layer)")
@@ -838,6 +838,7 @@ def main():
         res, keep = measure(cfg, args.steps, args.warmup, hip)
         results[name] = res
         if args.work_out and name == names[0]:
+            os.makedirs(os.path.dirname(os.path.abspath(args.work_out)), exist_ok=True)
             with open(args.work_out, "w") as f:
                 json.dump(dict(workload=name, wdtype=cfg.wdtype, steps=args.steps,
                                warmup=args.warmup, stage_work=res["stage_work"]), f, indent=1)

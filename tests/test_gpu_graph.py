@@ -58,3 +58,47 @@ def test_forward_graph_replays_match_eager(name, T, wdtype):
         torch.cuda.synchronize()
         for k in ("y", "idx", "gate", "counts"):
             assert torch.equal(got[k], ref[k]), (j, k)
+
+
+def test_zero_token_calls_graph_replays():
+    # With no tokens the forward zeroes the counts and the backward the weight
+    # gradients, by kernels (no memset node): captured once, every replay
+    # zeroes them again after eager work has filled them in between.
+    cfg, L = layer("tiny")
+    shape = lcmoe.shape_of(cfg)
+    x0 = torch.empty(0, cfg.d, dtype=torch.bfloat16, device="cuda")
+    counts = torch.empty(cfg.n_experts, dtype=torch.int32, device="cuda")
+    N, I, d, E = cfg.n_ffn, cfg.inter, cfg.d, cfg.n_experts
+    grads = dict(dx=torch.empty(0, d, dtype=torch.float32, device="cuda"),
+                 dw_router=torch.empty(E, d, dtype=torch.float32, device="cuda"),
+                 dw13=torch.empty(N, 2 * I, d, dtype=torch.bfloat16, device="cuda"),
+                 dw2=torch.empty(N, d, I, dtype=torch.bfloat16, device="cuda"))
+    dy0 = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+    ws = lcmoe.workspace(shape, 0)
+
+    def calls():
+        lcmoe.forward(shape, x0, L["w_router"], L["bias"], L["w13"], L["w2"], ws=ws,
+                      out=dict(counts=counts))
+        lcmoe.backward(shape, x0, L["w_router"], L["bias"], L["w13"], L["w2"], dy0, ws=ws,
+                       out=grads)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for fill in (7, -3):
+        counts.fill_(fill)
+        for k in ("dw_router", "dw13", "dw2"):
+            grads[k].fill_(fill)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(counts.abs().sum()) == 0
+        for k in ("dw_router", "dw13", "dw2"):
+            assert int(grads[k].abs().sum()) == 0, k
