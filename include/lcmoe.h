@@ -301,8 +301,11 @@ lcmoe_status lcmoe_bias_update(const lcmoe_shape* shape, int32_t t_all,
  * The weight-gradient GEMMs (dW2, dW13; HBM writes) run on the library's
  * second stream, on part of the CUs, beside dx and the router gradients
  * (HBM reads) on `stream`; the call joins them back before returning, so
- * the outputs are ordered on `stream` like any other work. The staged
- * variant runs every stage in order on `stream` (same kernels, same bits). */
+ * the outputs are ordered on `stream` like any other work. The first call
+ * on a device creates that stream and its two events (LCMOE_ERR_HIP if that
+ * fails), so under HIP graph capture make one call before capturing; the
+ * fork and join are then captured like the kernels. The staged variant runs
+ * every stage in order on `stream` (same kernels, same bits). */
 size_t lcmoe_backward_workspace_bytes(const lcmoe_shape* shape, int32_t max_tokens);
 lcmoe_status lcmoe_backward(const lcmoe_shape* shape, int32_t T, const void* x_bf16,
                             const float* w_router, const float* bias, const void* w13,

@@ -206,6 +206,9 @@ lcmoe_status aux_stream(AuxStream** out) {
     if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (j != nullptr) (void)hipEventDestroy(j);
+      if (f != nullptr) (void)hipEventDestroy(f);
+      if (s != nullptr) (void)hipStreamDestroy(s);
       (void)hipGetLastError();
       return LCMOE_ERR_HIP;
     }

@@ -102,3 +102,52 @@ def test_zero_token_calls_graph_replays():
         assert int(counts.abs().sum()) == 0
         for k in ("dw_router", "dw13", "dw2"):
             assert int(grads[k].abs().sum()) == 0, k
+
+
+def test_backward_graph_replays_match_eager():
+    # The backward forks its weight-gradient GEMMs onto the library's second
+    # stream and joins them back with events: captured once, the replays of
+    # that fork and join on new x and dy give the bits of eager calls.
+    cfg, L = layer("small")
+    shape = lcmoe.shape_of(cfg)
+    T = 700
+    xs = [inputs.make_tokens(cfg.with_(seed=cfg.seed + 3 * j), "cuda", tokens=T) for j in range(3)]
+    dys = [inputs.make_upstream_grad(cfg.with_(seed=cfg.seed + 3 * j), "cuda", tokens=T)
+           for j in range(3)]
+    x_in, dy_in = xs[0].clone(), dys[0].clone()
+    N, I, d, E = cfg.n_ffn, cfg.inter, cfg.d, cfg.n_experts
+
+    def grads():
+        return dict(dx=torch.empty(T, d, dtype=torch.float32, device="cuda"),
+                    dw_router=torch.empty(E, d, dtype=torch.float32, device="cuda"),
+                    dw13=torch.empty(N, 2 * I, d, dtype=torch.bfloat16, device="cuda"),
+                    dw2=torch.empty(N, d, I, dtype=torch.bfloat16, device="cuda"))
+
+    out = grads()
+    ws = torch.empty(lcmoe.backward_workspace_bytes(shape, T), dtype=torch.uint8, device="cuda")
+
+    def bwd(x, dy, ws_, out_):
+        return lcmoe.backward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"], dy, ws=ws_,
+                              out=out_)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bwd(x_in, dy_in, ws, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bwd(x_in, dy_in, ws, out)
+    torch.cuda.synchronize()
+    ws_eager = torch.empty_like(ws)
+    for j in (1, 0, 2, 1):
+        x_in.copy_(xs[j])
+        dy_in.copy_(dys[j])
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in out.items()}
+        ref = bwd(xs[j], dys[j], ws_eager, grads())
+        torch.cuda.synchronize()
+        for k in ("dx", "dw_router", "dw13", "dw2"):
+            assert torch.equal(got[k], ref[k]), (j, k)

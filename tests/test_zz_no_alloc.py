@@ -67,3 +67,42 @@ def test_noalloc_rejects_batches_past_the_array():
                           out=dict(counts=counts))
     torch.cuda.synchronize()
     assert int(counts.abs().sum()) == 0
+
+
+def test_noalloc_under_graph_capture():
+    # The callers it is for: work captured into a HIP graph. One call captured
+    # (no allocation, no memset, kernels only), then replayed on new token
+    # values written into the captured input, with eager work between
+    # replays; every replay gives the bits of an eager lcmoe_forward call.
+    cfg, L = layer("small")
+    shape = lcmoe.shape_of(cfg)
+    T = 300
+    xs = [inputs.make_tokens(cfg.with_(seed=cfg.seed + 5 * j), "cuda", tokens=T) for j in range(3)]
+    x_in = xs[0].clone()
+    out = dict(y=torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"),
+               idx=torch.empty(T, cfg.k, dtype=torch.int32, device="cuda"),
+               gate=torch.empty(T, cfg.k, dtype=torch.float32, device="cuda"),
+               counts=torch.empty(cfg.n_experts, dtype=torch.int32, device="cuda"))
+
+    def call():
+        lcmoe.forward_noalloc(shape, x_in, L["w_router"], L["bias"], L["w13"], L["w2"], out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for j in (1, 2, 0, 2):
+        x_in.copy_(xs[j])
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in out.items()}
+        ref = lcmoe.forward(shape, xs[j], L["w_router"], L["bias"], L["w13"], L["w2"])
+        torch.cuda.synchronize()
+        for k in ("y", "idx", "gate", "counts"):
+            assert torch.equal(got[k], ref[k]), (j, k)
