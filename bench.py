@@ -195,7 +195,7 @@ def trace_summary(trace_dir, workload, cmd, out_path, work_path=None):
         if st is None and "copyBuffer" not in name:
             continue
         short = name.split("(")[0].replace("void ", "")
-        lines.append(f"| `{short}` | {st or 'device copies (setup, calibration, backward x copies)'} | {r['Calls']} | "
+        lines.append(f"| `{short}` | {st or 'device copies (input setup and the copy calibration; no entry point of the layer enqueues one)'} | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     if work_path and os.path.exists(work_path):
