@@ -89,3 +89,37 @@ def test_fp8_config_bias_loop_stationary():
     means = np.array(means)
     print("mean FFN experts/token per step:", np.round(means, 4))
     assert np.all(np.abs(means - k_e) / k_e < 0.01)
+
+
+def test_bias_loop_resumes_from_saved_bias(tmp_path):
+    # The loop's only state is the caller's bias tensor (the library keeps
+    # nothing between calls): a run stopped after 60 steps, its bias saved to
+    # disk and loaded into a fresh tensor, continues exactly as the
+    # uninterrupted 120-step run, counts and bias bit for bit at every step.
+    cfg = inputs.CONFIGS["tiny"]
+    w, _ = inputs.make_router(cfg, "cuda")
+    shape = lcmoe.shape_of(cfg)
+    T, mu, k_e = 2048, 0.3, 2.5
+
+    def steps(bias, j0, j1, ws):
+        out = []
+        for j in range(j0, j1):
+            x = inputs.make_tokens(cfg, "cuda", stream=100 + j, tokens=T)
+            r = lcmoe.route(shape, x, w, bias, ws=ws)
+            lcmoe.bias_update(shape, r["counts"], mu, k_e, bias, T)
+            out.append((r["counts"].cpu().numpy().copy(), bias.cpu().numpy().copy()))
+        return out
+
+    ws = lcmoe.workspace(shape, T)
+    whole = steps(torch.zeros(cfg.n_experts, dtype=torch.float32, device="cuda"), 0, 120, ws)
+    b = torch.zeros(cfg.n_experts, dtype=torch.float32, device="cuda")
+    first = steps(b, 0, 60, ws)
+    path = tmp_path / "bias.pt"
+    torch.save(b.cpu(), path)
+    del b
+    resumed = torch.load(path, weights_only=True).to("cuda")
+    second = steps(resumed, 60, 120, lcmoe.workspace(shape, T))
+    for j, ((c0, b0), (c1, b1)) in enumerate(zip(whole, first + second)):
+        assert np.array_equal(c0, c1), j
+        assert np.array_equal(b0.view(np.uint32), b1.view(np.uint32)), j
+    assert not np.array_equal(whole[59][1], whole[119][1])  # the bias moved after the restart
