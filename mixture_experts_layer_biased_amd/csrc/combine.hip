@@ -13,48 +13,64 @@ namespace lcmoe {
 // input unchanged and costs no FLOPs):
 //   y_t = sum_k g_tk * v_tk,  v_tk = Y[row_of_slot(t,k)] for an FFN slot,
 //                             v_tk = x_t for a zero-computation slot,
-// accumulated in fp32 in k order, rounded once to bf16. One block per token,
-// 16-byte coalesced loads of whole rows.
+// accumulated in fp32 in k order, rounded once to bf16.
+//
+// A token's row is 16-byte chunks, one per thread; the threads of a token
+// are the chunk count rounded up to a power of two, 64 to 256. A 256-thread
+// block holds 1, 2 or 4 tokens (narrow rows fill the block). A row wider
+// than 256 chunks is walked by its threads in turn, or, for a batch under
+// 1,024 tokens, spread over gridDim.y blocks so that the batch covers the
+// chip (at 8,192 LongCat-shape tokens the spread form was 6% slower: the
+// three pieces of a 12 KB row are then read far apart in time). The rows of
+// four slots are requested together, then added in k order (eight at a time
+// measured 8% slower at that batch).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ Y,
                                                       const float* __restrict__ gate,
-                                                      const int* __restrict__ row_of_slot,
-                                                      int d, int K, uint16_t* __restrict__ y) {
-  __shared__ float sg[64];
-  __shared__ int srow[64];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < K) {
-    sg[tid] = gate[(size_t)t * K + tid];
-    srow[tid] = row_of_slot[(size_t)t * K + tid];
+                                                      const int* __restrict__ row_of_slot, int T,
+                                                      int d, int K, int tpt_log2,
+                                                      uint16_t* __restrict__ y) {
+  __shared__ float sg[256];  // tokens per block (<= 4) x K (<= 64)
+  __shared__ int srow[256];
+  const int tid = threadIdx.x;
+  const int tpt = 1 << tpt_log2, tpb = 256 >> tpt_log2;
+  const int t0 = blockIdx.x * tpb;
+  for (int i = tid; i < tpb * K; i += 256) {
+    const bool ok = t0 + i / K < T;
+    sg[i] = ok ? gate[(size_t)t0 * K + i] : 0.f;
+    srow[i] = ok ? row_of_slot[(size_t)t0 * K + i] : -1;
   }
   __syncthreads();
-  const int nch = d >> 3;
-  for (int c = tid; c < nch; c += 256) {
+  const int lt = tid >> tpt_log2;
+  const int t = t0 + lt;
+  if (t >= T) return;
+  const float* g = sg + lt * K;
+  const int* rows = srow + lt * K;
+  for (int c = blockIdx.y * tpt + (tid & (tpt - 1)); c < (d >> 3); c += tpt * gridDim.y) {
     const uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)t * d + 8 * c);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    // Four slots' rows are requested together, then added in k order.
     for (int k0 = 0; k0 < K; k0 += 4) {
       uint4 v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = k0 + j < K ? srow[k0 + j] : -1;
+        const int r = k0 + j < K ? rows[k0 + j] : -1;
         v[j] = r >= 0 ? *reinterpret_cast<const uint4*>(Y + (size_t)r * d + 8 * c) : xv;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (k0 + j >= K) break;
-        const float g = sg[k0 + j];
-        acc[0] += g * bf16_lo(v[j].x);
-        acc[1] += g * bf16_hi(v[j].x);
-        acc[2] += g * bf16_lo(v[j].y);
-        acc[3] += g * bf16_hi(v[j].y);
-        acc[4] += g * bf16_lo(v[j].z);
-        acc[5] += g * bf16_hi(v[j].z);
-        acc[6] += g * bf16_lo(v[j].w);
-        acc[7] += g * bf16_hi(v[j].w);
+        const float gk = g[k0 + j];
+        acc[0] += gk * bf16_lo(v[j].x);
+        acc[1] += gk * bf16_hi(v[j].x);
+        acc[2] += gk * bf16_lo(v[j].y);
+        acc[3] += gk * bf16_hi(v[j].y);
+        acc[4] += gk * bf16_lo(v[j].z);
+        acc[5] += gk * bf16_hi(v[j].z);
+        acc[6] += gk * bf16_lo(v[j].w);
+        acc[7] += gk * bf16_hi(v[j].w);
       }
     }
     uint4 o;
@@ -111,7 +127,12 @@ void launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
 
 void launch_combine(const uint16_t* x, const uint16_t* Y, const int* /*idx*/, const float* gate,
                     const int* row_of_slot, int T, int d, int K, uint16_t* y, hipStream_t s) {
-  combine_kernel<<<T, 256, 0, s>>>(x, Y, gate, row_of_slot, d, K, y);
+  const int nch = d / 8;
+  int lg = 6;  // threads per token: 64..256, at least the chunk count when it fits
+  while (lg < 8 && (1 << lg) < nch) ++lg;
+  const dim3 grid((unsigned)((T + (256 >> lg) - 1) / (256 >> lg)),
+                  T < 1024 ? (unsigned)((nch + (1 << lg) - 1) >> lg) : 1u);
+  combine_kernel<<<grid, 256, 0, s>>>(x, Y, gate, row_of_slot, T, d, K, lg, y);
 }
 
 void launch_bias_update(const int* counts, int N, int K, int t_all, double mu, double k_e,
