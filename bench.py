@@ -472,7 +472,45 @@ def measure(cfg, steps, warmup, hip):
     res["router_stats"] = dict(ms=st_ms, groups=D, algorithmic_bytes=st_bytes,
                                hbm_frac=st_bytes / (st_ms / 1e3) / PEAK_HBM)
     del r, sws
+    if "bias_steps" in cfg.extra:
+        res["bias_loop"] = bias_loop(cfg, L, shape, ws, out)
     return res, (L, x, out)
+
+
+def bias_loop(cfg, L, shape, ws, out):
+    """The bias-controller loop of a configuration that names one (the fp8
+    LongCat-shape batch: 20 steps, mu = 1e-3, K_e = 8): from the layer's
+    bias, each step runs lcmoe_forward on a fresh seeded batch (generator
+    stream 100 + j) and then lcmoe_bias_update with that call's counts.
+    Reports each step's mean FFN experts per token, the largest relative
+    deviation from K_e (the pages' convergence criterion is 1%), and the time
+    of the forward plus update (batch generation outside the timed pair)."""
+    import torch
+    from mixture_experts_layer_biased_amd import inputs, lcmoe
+
+    mu, k_e, n = cfg.extra["mu"], cfg.extra["k_e"], cfg.extra["bias_steps"]
+    T = cfg.tokens
+    bias = L["bias"].clone()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    means, ms = [], []
+    for j in range(n):
+        xj = inputs.make_tokens(cfg, "cuda", stream=100 + j)
+        torch.cuda.synchronize()
+        a.record()
+        lcmoe.forward(shape, xj, L["w_router"], bias, L["w13"], L["w2"], L["w13_scale"],
+                      L["w2_scale"], ws=ws, out=out)
+        lcmoe.bias_update(shape, out["counts"], mu, k_e, bias, T)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+        means.append(float(out["counts"][: cfg.n_ffn].sum().item()) / T)
+        del xj
+    dev = float(np.max(np.abs(np.array(means) - k_e)) / k_e)
+    return dict(steps=n, mu=mu, k_e=k_e, mean_ffn_experts_per_token=means,
+                max_rel_deviation=dev, within_1pct=dev < 0.01,
+                step_ms_median=float(np.median(ms)),
+                bias_ffn_absmax=float(bias[: cfg.n_ffn].abs().max().item()))
 
 
 def measure_small(steps, warmup):
@@ -854,6 +892,13 @@ def main():
               f"{res['tokens_per_s']:.0f} tok/s, dominant {res['dominant_kernel']} "
               f"{res['roofline']['frac']:.3f} of {res['roofline']['bound']}; router stats "
               f"{res['router_stats']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        if "bias_loop" in res:
+            bl = res["bias_loop"]
+            print(f"[bench] {name} bias loop: {bl['steps']} steps (mu={bl['mu']}, K_e={bl['k_e']}), "
+                  f"mean FFN experts/token {min(bl['mean_ffn_experts_per_token']):.4f}.."
+                  f"{max(bl['mean_ffn_experts_per_token']):.4f}, max deviation "
+                  f"{100 * bl['max_rel_deviation']:.2f}% (within 1%: {bl['within_1pct']}), "
+                  f"forward + update {bl['step_ms_median']:.3f} ms/step", file=sys.stderr, flush=True)
         if name == names[0] and not args.no_cpu_baseline:
             baseline = cpu_baseline(cfg, keep[0], keep[1], keep[2], args.cpu_experts)
         if name == "prefill" and not args.no_backward:
