@@ -850,7 +850,8 @@ def main():
                         os.path.join(ROOT, "profiles", f"counters_{args.workload}.md"))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark measures one GPU (the layer has no multi-GPU path "
+                                   "here); --gpus must be 1"}))
         sys.exit(2)
 
     import torch
