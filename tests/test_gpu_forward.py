@@ -147,27 +147,39 @@ def test_forward_longcat_shape_every_expert(name, n_sample, n_skew):
     check_rows(cfg, L, x, res, toks)
 
 
-def test_forward_maximum_tokens():
+@pytest.mark.parametrize("name", ["prefill", "fp8", "fp8a8"])
+def test_forward_maximum_tokens(name):
     # The largest batch the boundary accepts at the LongCat shape: the
-    # large-M GEMM addresses gathered x rows with 32-bit byte offsets, so
-    # T * d * 2 < 2^32 gives T = 349,525 (about 5,500 rows per FFN expert,
-    # 18 M-tiles each). The last tokens (x offsets just under 4 GiB) are
-    # checked along with the first; one token more is rejected.
-    cfg, L = layer("prefill")
+    # large-M GEMMs address gathered x rows (bf16, or fp8 codes with fp8
+    # activations) with 32-bit byte offsets, so T * d * 2 < 2^32 gives
+    # T = 349,525 (about 5,500 rows per FFN expert, 18 M-tiles each). The
+    # last tokens (x offsets just under 4 GiB) are checked along with the
+    # first, for bf16 weights, fp8 weights and fp8 weights and activations
+    # (stage by stage, through lcmoe_forward_inspect only: its equality with
+    # lcmoe_forward is checked at the other sizes); one token more is
+    # rejected.
+    cfg, L = layer(name)
     T = (2 ** 32 - 1) // (cfg.d * 2)
     shape = lcmoe.shape_of(cfg)
     x = inputs.make_tokens(cfg, "cuda", tokens=T, skew=False)
-    res = run_forward(cfg, L, x)
+    if cfg.wdtype == "fp8a8":
+        res = lcmoe.forward_inspect(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"],
+                                    L["w13_scale"], L["w2_scale"])
+        torch.cuda.synchronize()
+    else:
+        res = run_forward(cfg, L, x)
     counts = res["counts"].cpu().numpy()
     assert counts.sum() == T * cfg.k
-    print(f"T={T}: FFN slots {counts[:cfg.n_ffn].sum()}, max rows {counts[:cfg.n_ffn].max()}")
+    print(f"{name} T={T}: FFN slots {counts[:cfg.n_ffn].sum()}, max rows {counts[:cfg.n_ffn].max()}")
     check_rows(cfg, L, x, res, np.array([0, 1, T // 2, T - 2, T - 1]))
     del res
     torch.cuda.empty_cache()
     # T + 1 tokens: UNSUPPORTED before anything is read or enqueued
     p = [t.data_ptr() for t in (x, L["w_router"], L["bias"], L["w13"], L["w2"])]
-    st = lcmoe.lib().lcmoe_forward(ctypes.byref(shape), T + 1, p[0], p[1], p[2], p[3], None, p[4],
-                                   None, p[0], p[0], p[0], p[0], p[0], 1 << 40, None)
+    s13 = L["w13_scale"].data_ptr() if L["w13_scale"] is not None else None
+    s2 = L["w2_scale"].data_ptr() if L["w2_scale"] is not None else None
+    st = lcmoe.lib().lcmoe_forward(ctypes.byref(shape), T + 1, p[0], p[1], p[2], p[3], s13, p[4],
+                                   s2, p[0], p[0], p[0], p[0], p[0], 1 << 40, None)
     assert st == lcmoe.ERR_UNSUPPORTED
     del x
     torch.cuda.empty_cache()
