@@ -267,6 +267,56 @@ def test_backward_longcat_shape(name):
     assert err_r < 1e-3
 
 
+def test_backward_slot_buffers_past_4gib():
+    # The LongCat shape at T = 65,536 (about 524k FFN slot rows): the gathered
+    # slot-row buffers (x and dy rows, 6.4 GB each; the fp32 dX rows, 12.9 GB)
+    # pass 4 GiB, so the later experts' rows sit past 2^32 bytes from the
+    # buffer start and are reached through each expert's 64-bit base. dx on
+    # tokens whose slot rows lie there, and dW13/dW2 of the first touched
+    # expert and of the last two, against the oracle.
+    cfg, L = layer("prefill")
+    T = 65536
+    x = inputs.make_tokens(cfg, "cuda", tokens=T)
+    dy = inputs.make_upstream_grad(cfg, "cuda", tokens=T)
+    res = run_backward(cfg, L, x, dy)
+    idx = gpu_selection(cfg, L, x)
+    counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)[: cfg.n_ffn]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    row_bytes = cfg.d * 2
+    touched = np.nonzero(counts)[0]
+    pick = [int(touched[0]), int(touched[-2]), int(touched[-1])]
+    assert offsets[pick[1]] * row_bytes >= 2 ** 32  # rows past 4 GiB in the x and dy slot buffers
+    # tokens with a slot on the last touched expert (rows past 4 GiB), plus the first token
+    t_last = np.nonzero((idx == pick[-1]).any(1))[0]
+    toks = np.array(sorted(set([0] + t_last[:: max(1, len(t_last) // 4)][:4].tolist())))
+    ref = oracle_backward(cfg, L, x[torch.as_tensor(toks, device="cuda")],
+                          dy[torch.as_tensor(toks, device="cuda")], idx[toks])
+    err_dx = max_rel_err(res["dx"][torch.as_tensor(toks, device="cuda")].cpu().numpy(), ref["dx"])
+    get = expert_getter(L, "bf16", prefetch=pick)
+    wr = L["w_router"].cpu().numpy()
+    errs = {}
+    for e in pick:
+        rows, ks = np.nonzero(idx == e)
+        xv = bf16_values(x[torch.as_tensor(rows, device="cuda")])
+        dyv = bf16_values(dy[torch.as_tensor(rows, device="cuda")])
+        z = oracle.router_logits(xv, wr)
+        g, _ = oracle.softmax_gates(z, idx[rows])
+        w13_e, w2_e = get(e)
+        ge = g[np.arange(len(rows)), ks]
+        _, dw13, dw2, _ = oracle.expert_backward(xv, ge, dyv, w13_e, w2_e)
+        got13 = bf16_values(res["dw13"][e])
+        errs[(e, "dw13")] = TOL * dw13_excess(xv, dyv, ge, w13_e, w2_e, got13, dw13)
+        errs[(e, "dw2")] = max_rel_err(bf16_values(res["dw2"][e]), dw2)
+    worst = max(errs, key=errs.get)
+    print(f"T={T}: {int(counts.sum())} FFN slot rows; experts {pick} start at byte "
+          f"{[int(offsets[e] * row_bytes) for e in pick]} of the slot buffers; dx {err_dx:.3e} over "
+          f"{len(toks)} tokens; worst weight gradient {worst} {errs[worst]:.3e}")
+    assert err_dx < TOL
+    assert errs[worst] < TOL, (worst, errs[worst])
+    del res
+    torch.cuda.empty_cache()
+
+
 def test_backward_zero_tokens_and_determinism():
     cfg, L = layer("small")
     shape = lcmoe.shape_of(cfg)
