@@ -66,10 +66,8 @@ def source_hash():
 def stage_of_kernel(name):
     """Map a kernel symbol to its forward stage name."""
     if "gemm_big" in name:
-        return "gateup_large" if "<true" in name else "down_large"
-    if "gemm_small" in name:
-        return "gateup_small" if "<true" in name else "down_small"
-    if "quant_rows" in name:  # fp8 activations: x in the permute stage, H before down_small
+        return "gateup" if "<true" in name else "down"
+    if "quant_rows" in name:  # fp8 activations: x in the permute stage, H in the down stage
         return "quant (fp8 activations)"
     if "stats_partial" in name or "stats_final" in name:
         return "router statistics (outside the layer step)"
@@ -339,8 +337,8 @@ def kernel_work(cfg, counts, idx=None):
 
     What the method must move: each touched expert's weights read once (bf16
     2 B, fp8 1 B plus the 128x128 block scales), and for gate/up the token
-    rows that feed it read once (the distinct tokens with a slot on that
-    path; every token when idx is not given). The gathered per-slot copies of
+    rows that feed it read once (the distinct tokens with an FFN slot;
+    every token when idx is not given). The gathered per-slot copies of
     those rows, H and Y are the implementation's intermediates: reported as
     spill_bytes, not counted. Flops 2 * rows * (weights per expert).
     """
@@ -348,23 +346,20 @@ def kernel_work(cfg, counts, idx=None):
     c = counts[:N].astype(np.int64)
     sw = 1 if cfg.wdtype in ("fp8", "fp8a8") else 2
     sc = (4 / (128 * 128)) if cfg.wdtype in ("fp8", "fp8a8") else 0.0
-    out = {}
-    for path, sel in (("small", (c >= 1) & (c <= 32)), ("large", c > 32)):
-        et, rows = int(sel.sum()), int(c[sel].sum())
-        if idx is None:
-            toks = cfg.tokens if rows else 0
-        else:
-            on_path = np.isin(idx, np.nonzero(sel)[0])
-            toks = int(on_path.any(axis=1).sum())
-        out[f"gateup_{path}"] = dict(
-            bytes=et * 2 * I * d * (sw + sc) + toks * d * 2,
-            spill_bytes=max(rows - toks, 0) * d * 2 + rows * I * 2,
-            flops=2.0 * rows * 2 * I * d, experts=et, rows=rows)
-        out[f"down_{path}"] = dict(
-            bytes=et * d * I * (sw + sc),
-            spill_bytes=rows * I * 2 + rows * d * 2,
-            flops=2.0 * rows * I * d, experts=et, rows=rows)
-    return out
+    sel = c > 0
+    et, rows = int(sel.sum()), int(c.sum())
+    if idx is None:
+        toks = cfg.tokens if rows else 0
+    else:
+        toks = int((idx < N).any(axis=1).sum())
+    return {
+        "gateup": dict(bytes=et * 2 * I * d * (sw + sc) + toks * d * 2,
+                       spill_bytes=max(rows - toks, 0) * d * 2 + rows * I * 2,
+                       flops=2.0 * rows * 2 * I * d, experts=et, rows=rows),
+        "down": dict(bytes=et * d * I * (sw + sc),
+                     spill_bytes=rows * I * 2 + rows * d * 2,
+                     flops=2.0 * rows * I * d, experts=et, rows=rows),
+    }
 
 
 def layer_bytes(cfg, counts, T):
@@ -729,15 +724,14 @@ def copy_bandwidth(nbytes=4 << 30, reps=5):
 
 def vendor_gemm(cfg, counts, stages, reps=5):
     """The vendor library's dense batched product (torch.bmm, i.e. hipBLASLt)
-    at the large-path shape of the layer, next to the grouped kernels' own
-    figures: every expert of the large path (more than 32 routed rows) gets
-    the mean row count of those experts, rounded up to 32; bf16 operands
-    [batch][k][n] with a contiguous right operand; fp32 accumulation.
-    Context only: a dense product, with no row gather, no ragged row counts
-    and no SiLU epilogue. bf16 weights only."""
+    at the layer's grouped shape, next to the grouped kernels' own figures:
+    every touched expert gets the mean row count of the touched experts,
+    rounded up to 32; bf16 operands [batch][k][n] with a contiguous right
+    operand; fp32 accumulation. Context only: a dense product, with no row
+    gather, no ragged row counts and no SiLU epilogue. bf16 weights only."""
     import torch
     rows = counts[: cfg.n_ffn]
-    big = rows[rows > 32]
+    big = rows[rows > 0]
     if cfg.wdtype != "bf16" or big.size == 0:
         return None
     nb = int(big.size)
@@ -759,8 +753,8 @@ def vendor_gemm(cfg, counts, stages, reps=5):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         flops = 2.0 * nb * m * k * n
-        own = work[f"{name}_large"]
-        own_ms = stages[f"{name}_large"]
+        own = work[name]
+        own_ms = stages[name]
         out[name] = dict(vendor_ms=ms, vendor_tflops=flops / ms / 1e9,
                          vendor_frac=flops / (ms / 1e3) / PEAK_BF16,
                          grouped_ms=own_ms, grouped_tflops=own["flops"] / own_ms / 1e9,
@@ -823,7 +817,7 @@ def main():
                     help="measure only the backward on the prefill batch (for profiling runs)")
     ap.add_argument("--cpu-experts", type=int, default=240)
     ap.add_argument("--vendor-gemm", action="store_true",
-                    help="also time the vendor library's dense batched product at the large-path "
+                    help="also time the vendor library's dense batched product at the grouped "
                          "shape of each bf16 workload (context, not part of the layer)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="fold rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")

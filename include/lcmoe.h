@@ -235,12 +235,10 @@ typedef enum {
   LCMOE_STAGE_ROUTER = 0,     /* router logits                          */
   LCMOE_STAGE_TOPK = 1,       /* biased top-K and gates                 */
   LCMOE_STAGE_PERMUTE = 2,    /* histogram, scans, stable scatter        */
-  LCMOE_STAGE_GATEUP_SMALL = 3,  /* gate/up GEMM, experts with <= 32 rows */
-  LCMOE_STAGE_GATEUP_LARGE = 4,  /* gate/up GEMM, experts with > 32 rows  */
-  LCMOE_STAGE_DOWN_SMALL = 5,    /* down GEMM, experts with <= 32 rows    */
-  LCMOE_STAGE_DOWN_LARGE = 6,    /* down GEMM, experts with > 32 rows     */
-  LCMOE_STAGE_COMBINE = 7,    /* weighted combine + zero-expert identity */
-  LCMOE_NUM_STAGES = 8
+  LCMOE_STAGE_GATEUP = 3,     /* grouped gate/up GEMM with the SiLU gate */
+  LCMOE_STAGE_DOWN = 4,       /* grouped down GEMM                       */
+  LCMOE_STAGE_COMBINE = 5,    /* weighted combine + zero-expert identity */
+  LCMOE_NUM_STAGES = 6
 } lcmoe_stage;
 
 /* lcmoe_forward with stage timing for profiling harnesses: identical work,

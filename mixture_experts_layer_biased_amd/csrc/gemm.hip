@@ -7,17 +7,15 @@
 //   down:     Y = H W2^T                               [rows_e][d], bf16
 // with X_e the rows of x gathered through the expert's slots (perm).
 //
-// Two kernels, picked per expert on the device from its routed row count:
-//  * small-M (1..32 rows, decode batches): weights stream from HBM straight
-//    into MFMA A-operand registers (v_mfma_f32_16x16x32_bf16, weights as the
-//    16-row side, tokens as the 16-column side staged in LDS). Weight bytes
-//    dominate; every weight of a touched expert is read once.
-//  * large-M (33+ rows, prefill batches): M-tiles of up to 320 token rows
-//    (kBigTileRows) x 256 weight rows per block, 8 waves (2 x 4),
-//    v_mfma_f32_32x32x16_bf16, both operands copied HBM -> LDS by
-//    global_load_lds_dwordx4 in a multi-stage ring; the tiles of one expert
-//    (column slices, M-tiles) are adjacent on one XCD (blockIdx % 8) so its
-//    gathered x rows are shared through that XCD's L2.
+// Every expert with routed rows, decode batches included: M-tiles of up to
+// 320 token rows (kBigTileRows) x 256 weight rows per block, 8 waves (2 x 4),
+// v_mfma_f32_32x32x16_bf16, both operands copied HBM -> LDS by
+// global_load_lds_dwordx4 in a multi-stage ring; the tiles of one expert
+// (column slices, M-tiles) are adjacent on one XCD (blockIdx % 8) so its
+// gathered x rows are shared through that XCD's L2. With a handful of rows
+// (decode) the tile's MFMA work is small and the kernel is a stream of whole
+// 128-byte weight lines, which measured faster than streaming the weights
+// into MFMA operand registers (half-line requests) at every batch size.
 // fp8 (E4M3FN, one fp32 scale per 128x128 block) weights are converted in
 // registers: bf16(fl32(q) * s), then the same bf16 MFMA.
 #include <type_traits>
@@ -28,186 +26,6 @@
 namespace lcmoe {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
-
-// ===========================================================================
-// small-M kernel
-// ===========================================================================
-constexpr int kSmallLdsChunks = 4096;  // 64 KB of staged token rows
-// Token rows are staged with a pitch of 128, 256 or 1024 chunks (a multiple
-// of the 256-byte bank window), chunk c of row r at c ^ (r & 15): the 16
-// rows one MFMA operand read touches at the same chunk hit 16 distinct
-// slots. With up to 4 routed rows only 4 rows are staged (so one fill holds
-// 8192 k: all of k at the layer's shapes), and operand reads of rows 4..15,
-// whose results are never stored, read row 0.
-
-template <bool GATEUP, bool FP8>
-__global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
-  __shared__ uint4 sX[kSmallLdsChunks];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
-  const int total = a.meta[0] * a.nslices;
-  const int kdim = a.kdim;
-
-  for (int L = blockIdx.x; L < total; L += gridDim.x) {
-    const int e = a.small_list[L / a.nslices];
-    const int slice = L % a.nslices;
-    const int rows = a.counts[e];
-    const int row0 = a.offsets[e];
-    const int ncb = rows <= 16 ? 1 : 2;
-    const int rcap = rows <= 4 ? 4 : 16 * ncb;      // staged rows
-    const int kc = (kSmallLdsChunks * 8) / rcap;    // k elements per LDS fill
-    const int cpr = kc >> 3;                        // LDS row pitch (chunks)
-
-    // Two 16-row weight fragments per wave.
-    int fbase0, fbase1, ocol0;
-    if (GATEUP) {
-      ocol0 = slice * kSmallColsGateUp + wave * 16;
-      fbase0 = ocol0;             // gate rows
-      fbase1 = a.n_out + ocol0;   // matching up rows
-    } else {
-      ocol0 = slice * kSmallColsDown + wave * 32;
-      fbase0 = ocol0;
-      fbase1 = ocol0 + 16;
-    }
-    const bool active = ocol0 < a.n_out;  // n_out % 32 == 0: whole fragments valid
-
-    f32x4_t acc[2][2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[f][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const size_t wrow0 = (size_t)e * a.rows_total + (active ? fbase0 : 0) + lr;
-    const size_t wrow1 = (size_t)e * a.rows_total + (active ? fbase1 : 0) + lr;
-    const int sblk0 = (active ? fbase0 : 0) >> 7, sblk1 = (active ? fbase1 : 0) >> 7;
-
-    // Weight fragments for one 128-wide k step: four 16-byte loads per
-    // fragment (bf16), or two (fp8, 16 codes each).
-    auto load_w = [&](uint4 (&wv)[2][4], int kb) {
-      if (FP8) {
-        const uint8_t* w8 = static_cast<const uint8_t*>(a.w);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          wv[0][j] = *reinterpret_cast<const uint4*>(w8 + wrow0 * kdim + kb + 64 * j + 16 * lq);
-          wv[1][j] = *reinterpret_cast<const uint4*>(w8 + wrow1 * kdim + kb + 64 * j + 16 * lq);
-        }
-      } else {
-        const uint16_t* w16 = static_cast<const uint16_t*>(a.w);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int k = kb + 32 * s + 8 * lq;
-          if (kb + 32 * s < kdim) {
-            wv[0][s] = *reinterpret_cast<const uint4*>(w16 + wrow0 * kdim + k);
-            wv[1][s] = *reinterpret_cast<const uint4*>(w16 + wrow1 * kdim + k);
-          }
-        }
-      }
-    };
-    auto compute = [&](const uint4 (&wv)[2][4], int kb, int kc0) {
-      float sc0 = 1.f, sc1 = 1.f;
-      if (FP8) {
-        const int kblocks = kdim >> 7;
-        const size_t sbase = (size_t)e * (a.rows_total >> 7);
-        sc0 = a.wscale[(sbase + sblk0) * kblocks + (kb >> 7)];
-        sc1 = a.wscale[(sbase + sblk1) * kblocks + (kb >> 7)];
-      }
-      const int cb0 = (kb - kc0) >> 3;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (kb + 32 * s >= kdim) break;
-        bf16x8_t A0, A1;
-        int ch;
-        if (FP8) {
-          const int j = s >> 1, h = s & 1;
-          A0 = as_bf16x8(fp8x8_scaled_to_bf16x8(h ? wv[0][j].z : wv[0][j].x,
-                                                h ? wv[0][j].w : wv[0][j].y, sc0));
-          A1 = as_bf16x8(fp8x8_scaled_to_bf16x8(h ? wv[1][j].z : wv[1][j].x,
-                                                h ? wv[1][j].w : wv[1][j].y, sc1));
-          ch = cb0 + 8 * j + 2 * lq + h;
-        } else {
-          A0 = as_bf16x8(wv[0][s]);
-          A1 = as_bf16x8(wv[1][s]);
-          ch = cb0 + 4 * s + lq;
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          if (c < ncb) {
-            const int r = 16 * c + lr < rcap ? 16 * c + lr : 0;
-            const bf16x8_t B = as_bf16x8(sX[r * cpr + (ch ^ (r & 15))]);
-            acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[0][c], 0, 0, 0);
-            acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[1][c], 0, 0, 0);
-          }
-        }
-      }
-    };
-
-    uint4 w0[2][4], w1[2][4];
-    for (int kc0 = 0; kc0 < kdim; kc0 += kc) {
-      const int kcl = min(kc, kdim - kc0);
-      const int ccl = kcl >> 3;
-      const int kend = kc0 + kcl;
-      // The fill's first two weight steps are requested before its token
-      // rows are staged, so the weight stream runs on through the staging.
-      if (active) {
-        load_w(w0, kc0);
-        if (kc0 + 128 < kend) load_w(w1, kc0 + 128);
-      }
-      __syncthreads();  // previous LDS fill fully consumed
-      for (int id = tid; id < rows * ccl; id += 256) {
-        const int r = id / ccl, c = id - r * ccl;
-        const uint16_t* srow;
-        if (GATEUP)
-          srow = a.src + (size_t)(a.perm[row0 + r] / a.topk) * kdim;
-        else
-          srow = a.src + (size_t)(row0 + r) * kdim;
-        sX[r * cpr + (c ^ (r & 15))] = *reinterpret_cast<const uint4*>(srow + kc0 + 8 * c);
-      }
-      __syncthreads();
-      if (active) {
-        for (int kb = kc0; kb < kend; kb += 256) {
-          compute(w0, kb, kc0);
-          if (kb + 256 < kend) load_w(w0, kb + 256);
-          if (kb + 128 < kend) {
-            compute(w1, kb + 128, kc0);
-            if (kb + 384 < kend) load_w(w1, kb + 384);
-          }
-        }
-      }
-    }
-
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r = 16 * c + lr;
-        if (c < ncb && r < rows) {
-          if (GATEUP) {
-            const int col = ocol0 + 4 * lq;
-            float h[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) h[v] = silu_f(acc[0][c][v]) * acc[1][c][v];
-            *reinterpret_cast<uint2*>(a.out + (size_t)(row0 + r) * a.n_out + col) =
-                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            if (!FP8 && a.usave != nullptr) {  // u = [a; c] for the backward
-              float* u = a.usave + (size_t)(row0 + r) * 2 * a.n_out;
-              *reinterpret_cast<float4*>(u + col) =
-                  make_float4(acc[0][c][0], acc[0][c][1], acc[0][c][2], acc[0][c][3]);
-              *reinterpret_cast<float4*>(u + a.n_out + col) =
-                  make_float4(acc[1][c][0], acc[1][c][1], acc[1][c][2], acc[1][c][3]);
-            }
-          } else {
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-              const int col = ocol0 + 16 * f + 4 * lq;
-              *reinterpret_cast<uint2*>(a.out + (size_t)(row0 + r) * a.n_out + col) =
-                  make_uint2(pack_bf16x2(acc[f][c][0], acc[f][c][1]),
-                             pack_bf16x2(acc[f][c][2], acc[f][c][3]));
-            }
-          }
-        }
-      }
-    }
-  }
-}
 
 // ===========================================================================
 // large-M kernel: direct-to-LDS pipeline (bf16 or fp8 weights)
@@ -965,16 +783,6 @@ __global__ __launch_bounds__(512) void gemm_big_a8_kernel(GemmArgs a) {
 // ===========================================================================
 // launchers
 // ===========================================================================
-void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s) {
-  if (gateup) {
-    if (fp8) gemm_small_kernel<true, true><<<grid, 256, 0, s>>>(a);
-    else gemm_small_kernel<true, false><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (fp8) gemm_small_kernel<false, true><<<grid, 256, 0, s>>>(a);
-    else gemm_small_kernel<false, false><<<grid, 256, 0, s>>>(a);
-  }
-}
-
 void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s) {
   if (gateup) {
     if (fp8) gemm_big_dma_kernel<true, true><<<grid, 512, 0, s>>>(a);

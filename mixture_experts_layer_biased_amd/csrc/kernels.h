@@ -6,16 +6,12 @@
 
 namespace lcmoe {
 
-// Experts with 1..kSmallMaxRows routed rows run on the weight-streaming
-// (small-M) GEMM; larger ones on the LDS-tiled GEMM in M-tiles of at most
-// kBigTileRows rows (320 = mean 256 rows per expert at the fp8 batch plus
-// its spread, so those experts stream their weights once).
-constexpr int kSmallMaxRows = 32;
+// Every FFN expert with routed rows runs on the LDS-tiled grouped GEMM in
+// M-tiles of at most kBigTileRows rows (320 = mean 256 rows per expert at the
+// fp8 batch plus its spread, so those experts stream their weights once).
 constexpr int kBigTileRows = 320;
 
 // Grouped GEMM tile widths (output columns per block).
-constexpr int kSmallColsGateUp = 64;   // H columns per small gate/up block
-constexpr int kSmallColsDown = 128;    // Y columns per small down block
 constexpr int kBigColsGateUp = 128;    // H columns per large gate/up block
 constexpr int kBigColsDown = 256;      // Y columns per large down block
 
@@ -28,9 +24,8 @@ struct GemmArgs {
   const int* perm;         // FFN slot ids grouped by expert (gate/up gather)
   const int* offsets;      // [N+1]
   const int* counts;       // [E]
-  const int* small_list;   // experts on the small-M path
-  const int* mt_prefix;    // [N+1] M-tile prefix for the large-M path
-  const int* meta;         // [0] #small experts, [1] #large M-tiles, [2] S
+  const int* mt_prefix;    // [N+1] M-tile prefix over the FFN experts
+  const int* meta;         // [0] #touched FFN experts, [1] #M-tiles, [2] S
   uint16_t* out;           // gate/up: H [S][I]; down: Y [S][d]
   int kdim;                // reduction length (d or I)
   int n_out;               // output columns (I or d)
@@ -58,9 +53,8 @@ void launch_topk(const float* zpart, int ks, const float* bias, int T, int E, in
                  float* gate, float* logits_out, hipStream_t s);
 void launch_permute(const int* idx, int T, int K, int E, int N, int ntile,
                     unsigned long long* masks, int* tilecnt, int* tileoff, int* counts,
-                    int* offsets, int* small_list, int* mt_prefix, int* meta, int* perm,
+                    int* offsets, int* mt_prefix, int* meta, int* perm,
                     int* row_of_slot, hipStream_t s);
-void launch_gemm_small(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
 void launch_gemm_big(const GemmArgs& a, bool gateup, bool fp8, int grid, hipStream_t s);
 // The large-M gate/up GEMM with the backward epilogue (bf16 weights; every
 // expert with slots, M-tiles from mt_prefix, meta[1] = tile count).
@@ -68,11 +62,10 @@ void launch_gemm_big_bwd_u(const GemmArgs& a, int grid, hipStream_t s);
 // Large-M GEMM with fp8 weights and fp8 activations (src8, ascale).
 void launch_gemm_big_a8(const GemmArgs& a, bool gateup, int grid, hipStream_t s);
 // Per-row E4M3FN quantization of bf16 rows: q [rows][cols] codes, scale
-// [rows] = amax/448 (1 for a zero row), deq [rows][cols] bf16(fl32(q) * s)
-// (may alias src). The row count is read on the device (*rows_dev) when
-// rows_dev is not null, else `rows`; grid-stride over rows.
+// [rows] = amax/448 (1 for a zero row). The row count is read on the device
+// (*rows_dev) when rows_dev is not null, else `rows`; grid-stride over rows.
 void launch_quant_rows(const uint16_t* src, int rows, const int* rows_dev, int cols, uint8_t* q,
-                       float* scale, uint16_t* deq, int grid, hipStream_t s);
+                       float* scale, int grid, hipStream_t s);
 void launch_combine(const uint16_t* x, const uint16_t* Y, const int* idx, const float* gate,
                     const int* row_of_slot, int T, int d, int K, uint16_t* y, hipStream_t s);
 // Zero bytes [p, p + bytes) of a 4-byte aligned buffer (bytes % 4 == 0).

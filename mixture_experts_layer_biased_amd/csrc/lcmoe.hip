@@ -52,9 +52,9 @@ lcmoe_status noalloc_scratch(void** out) {
 struct Layout {
   int ks = 1, kchunk = 0, ntile = 0;
   long long smax = 0;
-  size_t zpart = 0, masks = 0, tilecnt = 0, tileoff = 0, offsets = 0, small_list = 0,
-         mt_prefix = 0, meta = 0, routing_end = 0, perm = 0, row_of_slot = 0, permute_end = 0,
-         H = 0, Y = 0, xq = 0, xs = 0, xdeq = 0, hq = 0, hs = 0, total = 0;
+  size_t zpart = 0, masks = 0, tilecnt = 0, tileoff = 0, offsets = 0, mt_prefix = 0,
+         meta = 0, routing_end = 0, perm = 0, row_of_slot = 0, permute_end = 0, H = 0, Y = 0,
+         xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
 };
 
 inline long long n_experts(const lcmoe_shape& s) { return (long long)s.n_ffn + s.n_zero; }
@@ -107,7 +107,6 @@ Layout make_layout(const lcmoe_shape& s, int T) {
   L.tilecnt = take((size_t)L.ntile * E * 4);
   L.tileoff = take((size_t)L.ntile * E * 4);
   L.offsets = take((size_t)(N + 1) * 4);
-  L.small_list = take((size_t)N * 4);
   L.mt_prefix = take((size_t)(N + 1) * 4);
   L.meta = take(64);
   L.routing_end = off;
@@ -118,11 +117,9 @@ Layout make_layout(const lcmoe_shape& s, int T) {
   L.H = take((size_t)L.smax * s.d_expert * 2);
   L.Y = take((size_t)L.smax * s.d_model * 2);
   if (s.w_dtype == LCMOE_W_FP8_E4M3_B128_A8) {
-    // fp8 activations: codes and per-row scales of x and of H, and the
-    // dequantized bf16 x the small-M path reads.
+    // fp8 activations: codes and per-row scales of x and of H.
     L.xq = take((size_t)T * s.d_model);
     L.xs = take((size_t)T * 4);
-    L.xdeq = take((size_t)T * s.d_model * 2);
     L.hq = take((size_t)L.smax * s.d_expert);
     L.hs = take((size_t)L.smax * 4);
   }
@@ -285,7 +282,7 @@ void enqueue_routing(const lcmoe_shape& s, int T, const Layout& L, char* base,
   launch_topk(zpart, L.ks, bias, T, E, s.top_k, idx, gate, logits_out, st);
   launch_permute(idx, T, s.top_k, E, s.n_ffn, L.ntile, at<unsigned long long>(base, L.masks),
                  at<int>(base, L.tilecnt), at<int>(base, L.tileoff), counts, offsets,
-                 at<int>(base, L.small_list), at<int>(base, L.mt_prefix), at<int>(base, L.meta),
+                 at<int>(base, L.mt_prefix), at<int>(base, L.meta),
                  perm, row_of_slot, st);
 }
 
@@ -350,7 +347,7 @@ lcmoe_status lcmoe_permute(const lcmoe_shape* shape, int32_t T, const int32_t* t
   clear_hip_error();
   launch_permute(topk_idx, T, shape->top_k, E, shape->n_ffn, L.ntile,
                  at<unsigned long long>(base, L.masks), at<int>(base, L.tilecnt),
-                 at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.small_list),
+                 at<int>(base, L.tileoff), counts, offsets,
                  at<int>(base, L.mt_prefix), at<int>(base, L.meta), perm, row_of_slot, stream);
   return hip_status();
 }
@@ -446,35 +443,31 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
     mark(ev, 2, stream);
     launch_permute(topk_idx, T, shape->top_k, E, shape->n_ffn, L.ntile,
                    at<unsigned long long>(base, L.masks), at<int>(base, L.tilecnt),
-                   at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.small_list),
-                   at<int>(base, L.mt_prefix), at<int>(base, L.meta), perm, row_of_slot, stream);
+                   at<int>(base, L.tileoff), counts, offsets, at<int>(base, L.mt_prefix),
+                   at<int>(base, L.meta), perm, row_of_slot, stream);
     if (a8)  // fp8 activations: quantize x per row (timed with the permutation stage)
       launch_quant_rows(static_cast<const uint16_t*>(x_bf16), T, nullptr, shape->d_model, xq, xs,
-                        at<uint16_t>(base, L.xdeq), std::min(2048, (T + 3) / 4), stream);
+                        std::min(2048, (T + 3) / 4), stream);
     mark(ev, 3, stream);
   }
 
   const int N = shape->n_ffn, d = shape->d_model, I = shape->d_expert;
   uint16_t* Y = at<uint16_t>(base, L.Y);
 
-  // Grid bounds from what the host knows (no device->host sync): at most
-  // min(N, S) experts on the small path and S/256 + #large experts M-tiles.
+  // Grid bound from what the host knows (no device->host sync): at most
+  // S/320 + min(N, S) M-tiles (each touched expert adds at most one partial
+  // tile to its share of S/320).
   const long long smax = L.smax;
-  const long long n_small_ub = std::min<long long>(N, smax);
-  const long long n_big_ub =
-      (smax + kBigTileRows - 1) / kBigTileRows + std::min<long long>(N, smax / (kSmallMaxRows + 1));
-  auto small_grid = [&](int nsl) {
-    return (int)std::max<long long>(1, std::min<long long>(n_small_ub * nsl, 512));
-  };
-  auto big_grid = [&](int nsl) {
-    const long long g = std::max<long long>(8, (n_big_ub * nsl + 7) / 8 * 8);
+  const long long n_tiles_ub =
+      (smax + kBigTileRows - 1) / kBigTileRows + std::min<long long>(N, smax);
+  auto grid_of = [&](int nsl) {
+    const long long g = std::max<long long>(8, (n_tiles_ub * nsl + 7) / 8 * 8);
     return (int)std::min<long long>(g, (1ll << 30));
   };
 
   GemmArgs a{};
   a.offsets = offsets;
   a.counts = counts;
-  a.small_list = at<int>(base, L.small_list);
   a.mt_prefix = at<int>(base, L.mt_prefix);
   a.meta = at<int>(base, L.meta);
   a.perm = perm;
@@ -484,9 +477,7 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   // gate/up: H = silu(X W1^T) * (X W3^T)
   a.w = w13;
   a.wscale = w13_scale;
-  // The small-M path reads bf16 activations: with fp8 activations, the
-  // dequantized rows fl32(q) * s rounded to bf16.
-  a.src = a8 ? at<uint16_t>(base, L.xdeq) : static_cast<const uint16_t*>(x_bf16);
+  a.src = static_cast<const uint16_t*>(x_bf16);
   a.src8 = xq;
   a.ascale = xs;
   a.out = Hpre;
@@ -494,15 +485,12 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   a.kdim = d;
   a.n_out = I;
   a.rows_total = 2 * I;
-  a.nslices = (I + kSmallColsGateUp - 1) / kSmallColsGateUp;
-  launch_gemm_small(a, true, fp8, small_grid(a.nslices), stream);
-  mark(ev, 4, stream);
   a.nslices = (I + kBigColsGateUp - 1) / kBigColsGateUp;
-  if (a8) launch_gemm_big_a8(a, true, big_grid(a.nslices), stream);
-  else launch_gemm_big(a, true, fp8, big_grid(a.nslices), stream);
-  mark(ev, 5, stream);
-  if (a8)  // quantize the S rows of H (S read on the device); dequantized bf16 copy into H
-    launch_quant_rows(Hpre, 0, at<int>(base, L.meta) + 2, I, hq, hs, H,
+  if (a8) launch_gemm_big_a8(a, true, grid_of(a.nslices), stream);
+  else launch_gemm_big(a, true, fp8, grid_of(a.nslices), stream);
+  mark(ev, 4, stream);
+  if (a8)  // quantize the S rows of H (S read on the device; timed with the down stage)
+    launch_quant_rows(Hpre, 0, at<int>(base, L.meta) + 2, I, hq, hs,
                       (int)std::min<long long>(2048, (smax + 3) / 4), stream);
 
   // down: Y = H W2^T
@@ -516,17 +504,14 @@ lcmoe_status forward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf1
   a.kdim = I;
   a.n_out = d;
   a.rows_total = d;
-  a.nslices = (d + kSmallColsDown - 1) / kSmallColsDown;
-  launch_gemm_small(a, false, fp8, small_grid(a.nslices), stream);
-  mark(ev, 6, stream);
   a.nslices = (d + kBigColsDown - 1) / kBigColsDown;
-  if (a8) launch_gemm_big_a8(a, false, big_grid(a.nslices), stream);
-  else launch_gemm_big(a, false, fp8, big_grid(a.nslices), stream);
-  mark(ev, 7, stream);
+  if (a8) launch_gemm_big_a8(a, false, grid_of(a.nslices), stream);
+  else launch_gemm_big(a, false, fp8, grid_of(a.nslices), stream);
+  mark(ev, 5, stream);
 
   launch_combine(static_cast<const uint16_t*>(x_bf16), Y, topk_idx, topk_gate, row_of_slot, T,
                  d, shape->top_k, static_cast<uint16_t*>(y_bf16), stream);
-  mark(ev, 8, stream);
+  mark(ev, 6, stream);
   return hip_status();
 }
 
@@ -694,7 +679,7 @@ lcmoe_status backward_impl(const lcmoe_shape* shape, int32_t T, const void* x_bf
   launch_topk(at<float>(base, L.zpart), L.ks, bias, T, E, K, idx, gate, logits, stream);
   launch_permute(idx, T, K, E, N, L.ntile, at<unsigned long long>(base, L.masks),
                  at<int>(base, L.tilecnt), at<int>(base, L.tileoff), counts, offsets,
-                 at<int>(base, L.small_list), at<int>(base, L.mt_prefix), at<int>(base, L.meta),
+                 at<int>(base, L.mt_prefix), at<int>(base, L.meta),
                  perm, row_of_slot, stream);
   launch_tile_prefix(counts, N, kBwdTileM, tprefix, nullptr, stream);
   int* bmeta = at<int>(base, B.bmeta);

@@ -13,14 +13,11 @@
 namespace lcmoe {
 
 // One wave per row (grid-stride): pass 1 takes the row's |max|, pass 2
-// quantizes eight values per lane step. Each 16-byte chunk is read and
-// written by the same lane, so deq may alias src (in-place dequantized
-// copy for the bf16 small-M path).
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* src, int rows,
+// quantizes eight values per lane step.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int rows,
                                                          const int* __restrict__ rows_dev,
                                                          int cols, uint8_t* __restrict__ q,
-                                                         float* __restrict__ scale,
-                                                         uint16_t* deq) {
+                                                         float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
   const int nrows = rows_dev != nullptr ? *rows_dev : rows;
   const int wpb = blockDim.x >> 6;
@@ -50,17 +47,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* src, in
       int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
       w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
       *reinterpret_cast<uint2*>(q + (size_t)r * cols + 8 * c) = make_uint2(w0, w1);
-      if (deq != nullptr)
-        *reinterpret_cast<uint4*>(deq + (size_t)r * cols + 8 * c) =
-            fp8x8_scaled_to_bf16x8((uint32_t)w0, (uint32_t)w1, s);
     }
     if (lane == 0) scale[r] = s;
   }
 }
 
 void launch_quant_rows(const uint16_t* src, int rows, const int* rows_dev, int cols, uint8_t* q,
-                       float* scale, uint16_t* deq, int grid, hipStream_t s) {
-  quant_rows_kernel<<<grid, 256, 0, s>>>(src, rows, rows_dev, cols, q, scale, deq);
+                       float* scale, int grid, hipStream_t s) {
+  quant_rows_kernel<<<grid, 256, 0, s>>>(src, rows, rows_dev, cols, q, scale);
 }
 
 }  // namespace lcmoe

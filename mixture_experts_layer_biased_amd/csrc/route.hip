@@ -236,9 +236,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
 //           the tile's count per expert (popcount), stored expert-major.
 //  colscan: per expert, exclusive prefix of the tile counts -> tile offsets,
 //           and the total T_i.
-//  schedule (one block): offsets over the FFN experts, the list of experts
-//           for the small-M GEMM path, and the M-tile prefix for the large-M
-//           path.
+//  schedule (one block): offsets over the FFN experts, the prefix of their
+//           M-tile counts for the grouped GEMMs, and the number of touched
+//           FFN experts.
 //  scatter: slot (t,k) with expert e < N goes to
 //           offsets[e] + tileoff[e][tile] + popcount(mask[tile][e] below t),
 //           i.e. ascending slot order inside each expert (stable).
@@ -303,9 +303,7 @@ __device__ int block_excl_scan_1024(int v, int* sh, int& total) {
 }
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ counts, int N,
-                                                        int small_max, int big_bm,
-                                                        int* __restrict__ offsets,
-                                                        int* __restrict__ small_list,
+                                                        int big_bm, int* __restrict__ offsets,
                                                         int* __restrict__ mt_prefix,
                                                         int* __restrict__ meta) {
   __shared__ int sh[40];
@@ -313,27 +311,23 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ 
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
   const int c0 = e0 < N ? counts[e0] : 0;
   const int c1 = e1 < N ? counts[e1] : 0;
-  const int f0 = (c0 >= 1 && c0 <= small_max), f1 = (c1 >= 1 && c1 <= small_max);
-  const int m0 = c0 > small_max ? (c0 + big_bm - 1) / big_bm : 0;
-  const int m1 = c1 > small_max ? (c1 + big_bm - 1) / big_bm : 0;
-  int tc, tf, tm;
+  const int m0 = (c0 + big_bm - 1) / big_bm, m1 = (c1 + big_bm - 1) / big_bm;  // 0 for no rows
+  int tc, tt, tm;
   const int xc = block_excl_scan_1024(c0 + c1, sh, tc);
-  const int xf = block_excl_scan_1024(f0 + f1, sh, tf);
+  block_excl_scan_1024((c0 > 0) + (c1 > 0), sh, tt);
   const int xm = block_excl_scan_1024(m0 + m1, sh, tm);
   if (e0 < N) {
     offsets[e0] = xc;
     mt_prefix[e0] = xm;
-    if (f0) small_list[xf] = e0;
   }
   if (e1 < N) {
     offsets[e1] = xc + c0;
     mt_prefix[e1] = xm + m0;
-    if (f1) small_list[xf + f0] = e1;
   }
   if (tid == 0) {
     offsets[N] = tc;
     mt_prefix[N] = tm;
-    meta[0] = tf;
+    meta[0] = tt;
     meta[1] = tm;
     meta[2] = tc;
   }
@@ -395,12 +389,11 @@ void launch_topk(const float* zpart, int ks, const float* bias, int T, int E, in
 
 void launch_permute(const int* idx, int T, int K, int E, int N, int ntile,
                     unsigned long long* masks, int* tilecnt, int* tileoff, int* counts,
-                    int* offsets, int* small_list, int* mt_prefix, int* meta, int* perm,
+                    int* offsets, int* mt_prefix, int* meta, int* perm,
                     int* row_of_slot, hipStream_t s) {
   hist_kernel<<<ntile, 256, (size_t)E * 8, s>>>(idx, T, K, E, ntile, masks, tilecnt);
   colscan_kernel<<<E, 64, 0, s>>>(tilecnt, tileoff, ntile, counts);
-  schedule_kernel<<<1, 1024, 0, s>>>(counts, N, kSmallMaxRows, kBigTileRows, offsets,
-                                     small_list, mt_prefix, meta);
+  schedule_kernel<<<1, 1024, 0, s>>>(counts, N, kBigTileRows, offsets, mt_prefix, meta);
   if (perm != nullptr)
     scatter_kernel<<<ntile, 256, 0, s>>>(idx, T, K, E, N, ntile, masks, tileoff, offsets, perm,
                                          row_of_slot);

@@ -24,9 +24,8 @@ EXPORTS = ("lcmoe_workspace_bytes", "lcmoe_route", "lcmoe_permute", "lcmoe_forwa
            "lcmoe_router_stats", "lcmoe_backward_workspace_bytes", "lcmoe_backward",
            "lcmoe_backward_staged", "lcmoe_forward_train", "lcmoe_backward_saved",
            "lcmoe_status_str")
-NUM_STAGES = 8
-STAGES = ("router", "topk", "permute", "gateup_small", "gateup_large", "down_small",
-          "down_large", "combine")
+NUM_STAGES = 6
+STAGES = ("router", "topk", "permute", "gateup", "down", "combine")
 
 
 class LcmoeError(RuntimeError):

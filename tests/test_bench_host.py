@@ -21,43 +21,44 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_forward_work_matches_the_layer_definition():
-    # every FFN slot on the large path: gate/up and down flops are 2 S 2I d
-    # and 2 S I d; weights of each touched expert are counted once
+    # gate/up and down flops are 2 S 2I d and 2 S I d; the weights of each
+    # touched expert are counted once
     cfg = inputs.CONFIGS["prefill"]
     counts = np.zeros(cfg.n_experts, dtype=np.int64)
     counts[: cfg.n_ffn] = 128
     w = bench.kernel_work(cfg, counts)
+    assert set(w) == {"gateup", "down"}
     S, d, I = 128 * cfg.n_ffn, cfg.d, cfg.inter
-    assert w["gateup_large"]["flops"] == 2.0 * S * 2 * I * d
-    assert w["down_large"]["flops"] == 2.0 * S * I * d
-    assert w["gateup_small"]["rows"] == 0 and w["down_small"]["flops"] == 0
+    assert w["gateup"]["flops"] == 2.0 * S * 2 * I * d
+    assert w["down"]["flops"] == 2.0 * S * I * d
     # algorithmic: the weights once and (gate/up) every token row once; the
     # per-slot gathered rows beyond that, H and Y are spills
-    assert w["gateup_large"]["bytes"] == cfg.n_ffn * 2 * I * d * 2 + cfg.tokens * d * 2
-    assert w["down_large"]["bytes"] == cfg.n_ffn * d * I * 2
-    assert w["gateup_large"]["spill_bytes"] == (S - cfg.tokens) * d * 2 + S * I * 2
-    assert w["down_large"]["spill_bytes"] == S * (I + d) * 2
-    # experts with 1..32 rows go to the small path, untouched experts cost nothing
+    assert w["gateup"]["bytes"] == cfg.n_ffn * 2 * I * d * 2 + cfg.tokens * d * 2
+    assert w["down"]["bytes"] == cfg.n_ffn * d * I * 2
+    assert w["gateup"]["spill_bytes"] == (S - cfg.tokens) * d * 2 + S * I * 2
+    assert w["down"]["spill_bytes"] == S * (I + d) * 2
+    # untouched experts cost nothing, however few rows the others have
     counts[:10] = 5
     counts[10:20] = 0
     w = bench.kernel_work(cfg, counts)
-    assert w["gateup_small"]["experts"] == 10 and w["gateup_large"]["experts"] == cfg.n_ffn - 20
+    assert w["gateup"]["experts"] == cfg.n_ffn - 10
+    assert w["gateup"]["rows"] == 10 * 5 + (cfg.n_ffn - 20) * 128
     lb = bench.layer_bytes(cfg, counts, cfg.tokens)
     assert lb == (cfg.n_ffn - 10) * 3 * I * d * 2 + cfg.n_experts * d * 4 + 2 * cfg.tokens * d * 2
 
 
-def test_forward_work_counts_distinct_tokens_per_path():
-    # with a routing given, gate/up reads each token row once per path that
-    # the token has a slot on
+def test_forward_work_counts_distinct_tokens():
+    # with a routing given, gate/up reads once each token row that has an
+    # FFN slot
     cfg = inputs.CONFIGS["tiny"].with_(n_ffn=4, n_zero=2, k=2, tokens=6)
     idx = np.array([[0, 4], [0, 1], [1, 5], [4, 5], [0, 2], [2, 0]])
     counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)   # [4, 2, 2, 0, 2, 2]
     w = bench.kernel_work(cfg, counts, idx)
-    assert w["gateup_small"]["rows"] == 8 and w["gateup_large"]["rows"] == 0
+    assert w["gateup"]["rows"] == 8 and w["gateup"]["experts"] == 3
     d, I = cfg.d, cfg.inter
     # tokens 0, 1, 2, 4, 5 have FFN slots; token 3 only zero experts
-    assert w["gateup_small"]["bytes"] == 3 * 2 * I * d * 2 + 5 * d * 2
-    assert w["gateup_small"]["spill_bytes"] == (8 - 5) * d * 2 + 8 * I * 2
+    assert w["gateup"]["bytes"] == 3 * 2 * I * d * 2 + 5 * d * 2
+    assert w["gateup"]["spill_bytes"] == (8 - 5) * d * 2 + 8 * I * 2
 
 
 def test_backward_work_counts_every_gradient_written():
@@ -78,9 +79,10 @@ def test_backward_work_counts_every_gradient_written():
 
 def test_stage_maps():
     assert bench.stage_of_kernel("void lcmoe::gemm_big_dma_kernel<true, false>(lcmoe::GemmArgs)") \
-        == "gateup_large"
-    assert bench.stage_of_kernel("void lcmoe::gemm_small_kernel<false, true>(lcmoe::GemmArgs)") \
-        == "down_small"
+        == "gateup"
+    assert bench.stage_of_kernel("void lcmoe::gemm_big_dma_kernel<false, true>(lcmoe::GemmArgs)") \
+        == "down"
+    assert bench.stage_of_kernel("void lcmoe::gemm_big_a8_kernel<false>(lcmoe::GemmArgs)") == "down"
     assert bench.stage_of_kernel("lcmoe::combine_kernel(unsigned short const*)") == "combine"
     assert bench.bwd_stage_of_kernel(
         "void lcmoe::bwd_dgrad_kernel<true, 3>(lcmoe::BwdGemmArgs)") == "dx_rows"

@@ -65,8 +65,8 @@ def check_routing_consistent(cfg, L, x, res):
 @pytest.mark.parametrize("name,T", [("tiny", 16), ("tiny", 1), ("tiny", 200), ("tiny", 777),
                                     ("small", 33), ("small", 300), ("small", 4096)])
 def test_forward_all_tokens(name, T):
-    # T spans the small-M path (few rows per expert), the mixed regime, and
-    # the large-M path with experts split into several M-tiles.
+    # T spans a few rows per expert (decode-like), the mixed regime, and
+    # experts split into several M-tiles.
     cfg, L = layer(name)
     x = inputs.make_tokens(cfg, "cuda", tokens=T)
     res = run_forward(cfg, L, x)
@@ -78,8 +78,8 @@ def test_forward_all_tokens(name, T):
 @pytest.mark.parametrize("T", [1, 33, 300, 4096])
 def test_forward_fp8_activations_all_tokens(T, inter):
     # fp8 weights and fp8 activations at the small shape, at every intermediate
-    # size from the smallest the boundary accepts (128): the small-M path
-    # (dequantized bf16 rows), the mixed regime and the large-M fp8-MFMA path.
+    # size from the smallest the boundary accepts (128), from a few rows per
+    # expert to several M-tiles, on the fp8-MFMA kernel.
     cfg, L = layer("small", wdtype="fp8a8", inter=inter)
     x = inputs.make_tokens(cfg, "cuda", tokens=T)
     res = run_forward(cfg, L, x)

@@ -48,14 +48,15 @@ def _id(c):
             f"-T{c['tokens']}")
 
 
-def test_cases_cover_both_paths_and_dtypes():
-    # the draw includes every weight type and batches on both GEMM paths
-    # (an expert with more than 32 expected routed rows: the large-M kernel)
+def test_cases_cover_dtypes_and_row_counts():
+    # the draw includes every weight type, batches with a few expected rows
+    # per expert (at most one 32-row fragment) and batches with several
+    # fragments per M-tile
     assert {c["wdtype"] for c in CASES} == {"bf16", "fp8", "fp8a8"}
     assert min(c["inter"] for c in CASES if c["wdtype"] == "fp8a8") < 384
-    big = [c for c in CASES
-           if c["tokens"] * c["k"] * c["n_ffn"] / (c["n_ffn"] + c["n_zero"]) / c["n_ffn"] > 32]
-    assert len(big) >= 2
+    rows = [c["tokens"] * c["k"] * c["n_ffn"] / (c["n_ffn"] + c["n_zero"]) / c["n_ffn"]
+            for c in CASES]
+    assert sum(r > 32 for r in rows) >= 2 and sum(r <= 32 for r in rows) >= 2
 
 
 @pytest.mark.gpu

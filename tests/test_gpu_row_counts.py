@@ -4,8 +4,9 @@ and backward, against the oracle.
 Routing is constructed (identity router, top-1, zero bias; see
 inputs.counted_routing_inputs) so that each expert receives an exact number
 of tokens. The FFN counts sit on either side of every size the kernels
-branch on: the small-M / large-M switch (32 rows), the large-M tile
-(320 rows, split evenly beyond) and its LDS ring (3 slots up to 168 rows),
+branch on: the 32-row MFMA fragments (a wave multiplies only the fragments
+that hold rows; a single row included), the grouped GEMM's M-tile (320
+rows, split evenly beyond) and its LDS ring (3 slots up to 168 rows),
 the dgrad M tile (256 rows) and its ring (3 slots up to 160 rows), the
 weight-gradient k stages (64 slot rows), and an FFN expert with no rows
 (zero weight gradients). d = 128 is narrower than one 256-column dgrad
