@@ -48,6 +48,21 @@ def test_library_has_no_undefined_internal_symbols():
     assert "lcmoe" not in out, out
 
 
+def test_binding_stages_match_the_header():
+    # the staged entry points write one event per stage boundary into a
+    # caller array of (stage count + 1): the binding's counts and names must
+    # be the header's enums, in order
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    fwd = dict((k, int(v)) for k, v in re.findall(r"\b(LCMOE_STAGE_[A-Z_]+|LCMOE_NUM_STAGES)\s*=\s*(\d+)", src))
+    assert fwd.pop("LCMOE_NUM_STAGES") == lcmoe.NUM_STAGES == len(lcmoe.STAGES)
+    names = [k[len("LCMOE_STAGE_"):].lower() for k, _ in sorted(fwd.items(), key=lambda kv: kv[1])]
+    assert sorted(fwd.values()) == list(range(lcmoe.NUM_STAGES))
+    assert names == list(lcmoe.STAGES)
+    # the backward's staged call documents its event count
+    n_bwd = int(re.search(r"recording the caller's (\d+) events", open(HEADER).read()).group(1))
+    assert n_bwd == lcmoe.NUM_BWD_STAGES + 1 == len(lcmoe.BWD_STAGES) + 1
+
+
 def test_status_strings():
     assert lcmoe.status_str(0) == "LCMOE_OK"
     assert lcmoe.status_str(3) == "LCMOE_ERR_WORKSPACE"

@@ -227,3 +227,36 @@ def test_forward_zero_tokens_and_determinism():
     b = run_forward(cfg, L, x)
     for k in ("y", "idx", "gate", "counts"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8a8"])
+def test_forward_staged_matches_and_records_every_stage(wdtype):
+    # lcmoe_forward_staged: the outputs of lcmoe_forward bit for bit, and one
+    # event per stage boundary (NUM_STAGES + 1 caller events), in order
+    cfg, L = layer("small", wdtype=wdtype)
+    x = inputs.make_tokens(cfg, "cuda", tokens=777)
+    shape = lcmoe.shape_of(cfg)
+    ref = lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"],
+                        L["w13_scale"], L["w2_scale"])
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    n = lcmoe.NUM_STAGES
+    ev = (ctypes.c_void_p * (n + 1))()
+    for i in range(n + 1):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        ev[i] = h
+    got = lcmoe.forward(shape, x, L["w_router"], L["bias"], L["w13"], L["w2"],
+                        L["w13_scale"], L["w2_scale"], stage_events=ev)
+    torch.cuda.synchronize()
+    for k in ("y", "idx", "gate", "counts"):
+        assert torch.equal(ref[k], got[k]), k
+    ms = ctypes.c_float()
+    for i in range(n):
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[i], ev[i + 1]) == 0
+        assert ms.value >= 0, lcmoe.STAGES[i]
+    for i in range(n + 1):
+        hip.hipEventDestroy(ev[i])
