@@ -1,6 +1,6 @@
 """Seeded random layer shapes through the C ABI, against the oracle.
 
-Shapes are drawn (fixed seed) inside the boundary's limits: d and I
+Thirty-six shapes are drawn (fixed seed) inside the boundary's limits: d and I
 multiples of 32 (of 128 with fp8 weights), 1..80 FFN and 0..48 zero experts,
 K from 1 to min(E, 16), T from 1 to 600 tokens, router bias of scale 0, 0.1
 or 1, with or without the 1% of tokens scaled x20. Every case checks the
@@ -21,7 +21,7 @@ from tests.test_gpu_forward import check_routing_consistent, check_rows, run_for
 SEED = 20261203
 
 
-def _cases(n=24):
+def _cases(n=36):
     rng = np.random.default_rng(SEED)
     out = []
     for i in range(n):
