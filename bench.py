@@ -177,8 +177,9 @@ def trace_summary(trace_dir, workload, cmd, out_path, work_path=None):
     kernels (calls, average / min / max duration) as a markdown table. With
     the work file the profiled bench run wrote (--work-out), also each
     grouped-GEMM stage's roofline fraction from the rocprof durations of the
-    timed launches (the last `steps` dispatches of its kernel), next to the
-    bench's own event timing of the same launches."""
+    timed launches (the `steps` dispatches of its kernel before the
+    `trailing` ones the run made after its timed loop), next to the bench's
+    own event timing of the same launches."""
     import csv
     mapper = bwd_stage_of_kernel if workload.startswith("backward") else stage_of_kernel
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
@@ -216,7 +217,9 @@ def trace_summary(trace_dir, workload, cmd, out_path, work_path=None):
         for st, w in work["stage_work"].items():
             if st not in durs or w["flops"] == 0:
                 continue
-            d = [x[1] for x in sorted(durs[st])][-steps:]
+            seq = [x[1] for x in sorted(durs[st])]
+            tail = int(work.get("trailing", 0))
+            d = seq[max(0, len(seq) - tail - steps):len(seq) - tail]
             ms = float(np.mean(d)) / 1e6
             peak_m = PEAK_FP8 if work["wdtype"] == "fp8a8" else PEAK_BF16
             bound = "hbm" if w["flops"] / max(w["bytes"], 1) < peak_m / PEAK_HBM else "mfma"
@@ -873,8 +876,11 @@ def main():
         if args.work_out and name == names[0]:
             os.makedirs(os.path.dirname(os.path.abspath(args.work_out)), exist_ok=True)
             with open(args.work_out, "w") as f:
+                # trailing: layer calls made after the timed loop (the bias
+                # loop's forwards), which the trace summary leaves out
                 json.dump(dict(workload=name, wdtype=cfg.wdtype, steps=args.steps,
-                               warmup=args.warmup, stage_work=res["stage_work"]), f, indent=1)
+                               warmup=args.warmup, trailing=int(cfg.extra.get("bias_steps", 0)),
+                               stage_work=res["stage_work"]), f, indent=1)
         if args.vendor_gemm:
             res["vendor_gemm"] = vendor_gemm(cfg, keep[2]["counts"].cpu().numpy(), res["stages_ms"])
             if res["vendor_gemm"]:
