@@ -201,12 +201,18 @@ def trace_summary(trace_dir, workload, cmd, out_path, work_path=None):
         work = json.load(open(work_path))
         steps = int(work["steps"])
         trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+        trace.sort(key=lambda r: int(r["Start_Timestamp"]))
         durs = {}
+        prev = None  # (stage, duration) of the dispatch before this one
         for r in trace:
             st = mapper(r["Kernel_Name"])
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             if st is not None:
-                durs.setdefault(st, []).append(
-                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+                # with fp8 activations the down stage begins with the
+                # quantization of H (the dispatch right before it)
+                extra = prev[1] if st == "down" and prev and prev[0] == "quant (fp8 activations)" else 0
+                durs.setdefault(st, []).append((int(r["Start_Timestamp"]), dur + extra))
+            prev = (st, dur)
         lines += ["", f"Roofline of the grouped-GEMM stages over the {steps} timed launches "
                   "(algorithmic bytes: touched experts' weights once, plus the token rows once for "
                   "gate/up; spills are the gathered per-slot rows, H and Y; peaks 8 TB/s HBM, "
